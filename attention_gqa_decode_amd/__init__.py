@@ -1,0 +1,216 @@
+"""Exact grouped-query attention forward for MI355X (gfx950): a thin binding of ``libattn_gqa.so``.
+
+Every function here only marshals arguments into the C ABI declared in
+``include/attn_gqa.h`` (same names); all arithmetic runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  If the library is missing the
+calls raise ``RuntimeError``: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_gqa.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_UNSUPPORTED = -3
+ATTN_ERR_ALIGN = -4
+ATTN_ERR_WORKSPACE = -5
+ATTN_ERR_HIP = -6
+ATTN_MAX_BATCH = 256
+ATTN_MAX_GROUP = 16
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class attn_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("q", _P), ("k_cache", _P), ("v_cache", _P), ("seqlens", _P), ("out", _P),
+        ("B", _I), ("Hq", _I), ("KH", _I), ("Hsz", _I),
+        ("kv_stride", _I64), ("scale", ctypes.c_float),
+        ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+        ("tile_keys", _I), ("num_ctas", _I),
+        ("ev_tiles_begin", _P), ("ev_tiles_end", _P),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_gqa_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.attn_decode.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
+    L.attn_decode.restype = _I
+    L.attn_decode_ex.argtypes = [ctypes.POINTER(attn_decode_args), _P]
+    L.attn_decode_ex.restype = _I
+    L.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_prefill_causal.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]
+    L.attn_prefill_causal.restype = _I
+    L.attn_decode_plan.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.attn_decode_plan.restype = _I
+    L.attn_hbm_copy_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    L.attn_hbm_copy_probe.restype = _I
+    L.attn_device_info.argtypes = [_P, _P]
+    L.attn_device_info.restype = _I
+    L.attn_release.argtypes = []
+    L.attn_release.restype = _I
+    L.attn_status_string.argtypes = [_I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        L = lib()
+        msg = L.attn_last_error().decode() or L.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bf16_cuda(name, t):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous bf16 CUDA tensor (got {t.dtype}, {t.device})")
+
+
+def _host_seqlens(seqlens):
+    import numpy as np
+    import torch
+    if isinstance(seqlens, torch.Tensor):
+        seqlens = seqlens.detach().cpu().numpy()
+    arr = np.ascontiguousarray(np.asarray(seqlens), dtype=np.int32)
+    return arr
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
+    """Decode step (``attn_decode``): q [B][Hq][Hsz], caches [B][KH][S][Hsz] bf16, S = max seqlens.
+
+    ``seqlens`` is a host sequence of int32 lengths.  Returns ``out`` fp32 [B][Hq][Hsz].
+    """
+    import torch
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _bf16_cuda(n, t)
+    B, Hq, Hsz = q.shape
+    KH, S = k_cache.shape[1], k_cache.shape[2]
+    sl = _host_seqlens(seqlens)
+    if len(sl) != B:
+        raise ValueError("seqlens must have B entries")
+    if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
+    if S != int(sl.max(initial=0)):
+        raise ValueError("attn_decode packs the cache to max(seqlens); use attn_decode_ex for another capacity")
+    if out is None:
+        out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
+    _check(lib().attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), sl.ctypes.data, B, Hq, KH, Hsz,
+                             out.data_ptr(), _stream_handle(stream)))
+    return out
+
+
+def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
+                   workspace=None, ev_tiles_begin=None, ev_tiles_end=None, stream=None):
+    """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
+
+    ``workspace`` is an optional CUDA tensor used as the partial-state buffer;
+    ``ev_tiles_begin/end`` are optional raw ``hipEvent_t`` handles (ints).
+    """
+    import torch
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _bf16_cuda(n, t)
+    B, Hq, Hsz = q.shape
+    KH, S = k_cache.shape[1], k_cache.shape[2]
+    sl = _host_seqlens(seqlens)
+    if len(sl) != B:
+        raise ValueError("seqlens must have B entries")
+    if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
+    if out is None:
+        out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
+    a = attn_decode_args()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
+    a.kv_stride = S
+    a.scale = float(scale)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+    a.ev_tiles_begin = ev_tiles_begin
+    a.ev_tiles_end = ev_tiles_end
+    _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
+    return out
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, KH: int, Hsz: int, num_ctas: int = 0) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, KH, Hsz, num_ctas))
+
+
+def attn_prefill_causal(q, k, v, out=None, stream=None):
+    """Causal prefill (``attn_prefill_causal``): q [B][Hq][ISL][Hsz], k/v [B][KH][ISL][Hsz] bf16 -> bf16."""
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _bf16_cuda(n, t)
+    B, Hq, ISL, Hsz = q.shape
+    KH = k.shape[1]
+    if k.shape != (B, KH, ISL, Hsz) or v.shape != k.shape:
+        raise ValueError("k/v must be [B][KH][ISL][Hsz]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().attn_prefill_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, ISL, Hq, KH, Hsz, out.data_ptr(),
+                                     _stream_handle(stream)))
+    return out
+
+
+def attn_decode_plan(seqlens, KH: int, tile_keys: int, num_ctas: int):
+    """Host planner (``attn_decode_plan``): returns (N, P, cta_tile_begin[P+1], seg_tile_begin[B*KH+1])."""
+    import numpy as np
+    sl = _host_seqlens(seqlens)
+    B = len(sl)
+    N = ctypes.c_int64()
+    P = ctypes.c_int()
+    cta = np.zeros(max(num_ctas, 0) + 1, dtype=np.int64)
+    seg = np.zeros(B * KH + 1, dtype=np.int64)
+    _check(lib().attn_decode_plan(sl.ctypes.data, B, KH, tile_keys, num_ctas, ctypes.byref(N), ctypes.byref(P),
+                                  cta.ctypes.data, seg.ctypes.data))
+    return N.value, P.value, cta[: P.value + 1], seg
+
+
+def attn_hbm_copy_probe(src, dst, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().attn_hbm_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream)))
+
+
+def attn_device_info():
+    cus, lds = ctypes.c_int(), ctypes.c_int()
+    _check(lib().attn_device_info(ctypes.byref(cus), ctypes.byref(lds)))
+    return cus.value, lds.value
+
+
+def attn_release():
+    _check(lib().attn_release())

@@ -1,0 +1,353 @@
+// api.hip -- the C ABI (include/attn_gqa.h): validation, LeanTile planning, workspace, launches.
+//
+// Every argument check runs before the first HIP runtime call, so argument
+// errors are reported synchronously and leave no trace on the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/attn_gqa.h"
+#include "common.h"
+
+static_assert(ATTN_MAX_GROUP == attn::kMaxGroup, "group limit mismatch");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int fail_hip(hipError_t e, const char *what) {
+    return fail(ATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;      // library-owned partial-state buffers
+std::map<std::pair<int, int>, int> g_default_ctas;          // (device, Hsz*64+G) -> resident CTAs
+
+int device_default_ctas(int Hsz, int G, int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto key = std::make_pair(dev, Hsz * 64 + G);
+    auto it = g_default_ctas.find(key);
+    if (it != g_default_ctas.end()) {
+        *out = it->second;
+        return ATTN_OK;
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    const int occ = attn::decode_tiles_occupancy(Hsz, G);
+    *out = g_default_ctas[key] = cus * occ;
+    return ATTN_OK;
+}
+
+int library_workspace(hipStream_t stream, size_t bytes, void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize(stream);  // earlier launches on this stream may still read it
+            if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+            e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+        }
+        size_t grow = bytes + bytes / 4;
+        e = hipMalloc(&w.ptr, grow);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return fail_hip(e, "hipMalloc(workspace)");
+        }
+        w.bytes = grow;
+    }
+    *ptr = w.ptr;
+    return ATTN_OK;
+}
+
+// Shape checks shared by attn_decode_ex and attn_decode_workspace_bytes.
+int check_decode_dims(int B, int Hq, int KH, int Hsz) {
+    if (B <= 0 || Hq <= 0 || KH <= 0) return fail(ATTN_ERR_SHAPE, "B, Hq and KH must be positive (B=%d Hq=%d KH=%d)", B, Hq, KH);
+    if (Hq % KH != 0) return fail(ATTN_ERR_SHAPE, "Hq=%d is not a multiple of KH=%d", Hq, KH);
+    if (Hsz != 64 && Hsz != 128 && Hsz != 256) return fail(ATTN_ERR_UNSUPPORTED, "Hsz=%d (supported: 64, 128, 256)", Hsz);
+    if (Hq / KH > attn::kMaxGroup) return fail(ATTN_ERR_UNSUPPORTED, "group size G=%d exceeds %d", Hq / KH, attn::kMaxGroup);
+    if (B > ATTN_MAX_BATCH) return fail(ATTN_ERR_UNSUPPORTED, "B=%d exceeds %d", B, ATTN_MAX_BATCH);
+    return ATTN_OK;
+}
+
+// Host half of the LeanTile plan: tile prefix over batches and the tile count N.
+int build_plan(const int32_t *seqlens, int B, int KH, int T, int64_t stride, LeanPlan *plan) {
+    plan->B = B;
+    plan->KH = KH;
+    plan->T = T;
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t L = seqlens[b];
+        if (L < 0) return fail(ATTN_ERR_SHAPE, "seqlens[%d]=%d is negative", b, L);
+        if (stride >= 0 && L > stride) return fail(ATTN_ERR_SHAPE, "seqlens[%d]=%d exceeds kv_stride=%lld", b, L, (long long)stride);
+        plan->seqlen[b] = L;
+        plan->tile_prefix[b] = (int32_t)acc;
+        acc += (int64_t)KH * ((L + (int64_t)T - 1) / T);
+        if (acc > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "too many LeanTiles (%lld); raise tile_keys", (long long)acc);
+    }
+    plan->tile_prefix[B] = (int32_t)acc;
+    plan->N = acc;
+    plan->P = 1;
+    return ATTN_OK;
+}
+
+bool any_split_segment(const LeanPlan &p) {
+    for (int b = 0; b < p.B; ++b) {
+        const int nb = plan_tiles_per_segment(p, b);
+        if (nb == 0) continue;
+        for (int kh = 0; kh < p.KH; ++kh) {
+            const int64_t s0 = p.tile_prefix[b] + (int64_t)kh * nb;
+            if (plan_cta_of_tile(p, s0) != plan_cta_of_tile(p, s0 + nb - 1)) return true;
+        }
+    }
+    return false;
+}
+
+bool any_empty_segment(const LeanPlan &p) {
+    for (int b = 0; b < p.B; ++b)
+        if (p.seqlen[b] == 0) return true;
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "null pointer argument";
+        case ATTN_ERR_SHAPE: return "inconsistent shape";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace too small";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas) {
+    if (check_decode_dims(B, Hq, KH, Hsz) != ATTN_OK || num_ctas < 0) return 0;
+    const int G = Hq / KH;
+    int P = num_ctas;
+    if (P == 0 && device_default_ctas(Hsz, G, &P) != ATTN_OK) return 0;
+    return (size_t)2 * P * attn::decode_slot_floats(G, Hsz) * sizeof(float);
+}
+
+int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
+    g_last_error.clear();
+    if (!a) return fail(ATTN_ERR_NULL, "args is NULL");
+    if (!a->q || !a->k_cache || !a->v_cache || !a->seqlens || !a->out)
+        return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, seqlens and out must be non-NULL");
+    int st = check_decode_dims(a->B, a->Hq, a->KH, a->Hsz);
+    if (st != ATTN_OK) return st;
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->out))
+        return fail(ATTN_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (a->kv_stride < 0) return fail(ATTN_ERR_SHAPE, "kv_stride=%lld is negative", (long long)a->kv_stride);
+    if (a->tile_keys < 0 || a->num_ctas < 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be >= 0");
+    if (!(a->scale == a->scale) || isinf(a->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
+    if (a->workspace && !aligned16(a->workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+    const int G = a->Hq / a->KH;
+    int64_t stride = a->kv_stride;
+    if (stride == 0) {
+        for (int b = 0; b < a->B; ++b) stride = a->seqlens[b] > stride ? a->seqlens[b] : stride;
+    }
+    const int T = a->tile_keys > 0 ? a->tile_keys : attn::kDefaultTileKeys;
+
+    attn::DecodeParams p;
+    st = build_plan(a->seqlens, a->B, a->KH, T, stride, &p.plan);
+    if (st != ATTN_OK) return st;
+    p.q = static_cast<const uint16_t *>(a->q);
+    p.k = static_cast<const uint16_t *>(a->k_cache);
+    p.v = static_cast<const uint16_t *>(a->v_cache);
+    p.out = a->out;
+    p.ws = nullptr;
+    p.kv_stride = stride;
+    p.Hq = a->Hq;
+    p.G = G;
+    p.slot_floats = attn::decode_slot_floats(G, a->Hsz);
+    const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Hsz);
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    int P = a->num_ctas;
+    if (P > 0 && a->workspace && (size_t)2 * P * p.slot_floats * sizeof(float) > a->workspace_bytes)
+        return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for num_ctas=%d", a->workspace_bytes,
+                    (size_t)2 * P * p.slot_floats * sizeof(float), P);
+
+    // ---- argument checks done; HIP calls from here on ----
+    if (P == 0) {
+        st = device_default_ctas(a->Hsz, G, &P);
+        if (st != ATTN_OK) return st;
+    }
+    if (p.plan.N > 0 && P > p.plan.N) P = (int)p.plan.N;
+    p.plan.P = P;
+
+    const bool split = p.plan.N > 0 && any_split_segment(p.plan);
+    if (split) {
+        const size_t need = (size_t)2 * P * p.slot_floats * sizeof(float);
+        if (a->workspace) {
+            if (a->workspace_bytes < need)
+                return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed", a->workspace_bytes, need);
+            p.ws = static_cast<float *>(a->workspace);
+        } else {
+            void *w = nullptr;
+            st = library_workspace(stream, need, &w);
+            if (st != ATTN_OK) return st;
+            p.ws = static_cast<float *>(w);
+        }
+    }
+
+    hipError_t e;
+    if (p.plan.N > 0) {
+        if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
+            return fail_hip(e, "hipEventRecord(begin)");
+        e = attn::launch_decode_tiles(p, a->Hsz, stream);
+        if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
+        if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
+            return fail_hip(e, "hipEventRecord(end)");
+    }
+    if (split || any_empty_segment(p.plan)) {
+        e = attn::launch_decode_merge(p, a->Hsz, stream);
+        if (e != hipSuccess) return fail_hip(e, "decode merge kernel launch");
+    }
+    return ATTN_OK;
+}
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B, int Hq,
+                int KH, int Hsz, float *out, hipStream_t stream) {
+    attn_decode_args a = {};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.seqlens = seqlens;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.KH = KH;
+    a.Hsz = Hsz;
+    return attn_decode_ex(&a, stream);
+}
+
+int attn_decode_plan(const int32_t *seqlens, int B, int KH, int tile_keys, int num_ctas, int64_t *N_out, int *P_out,
+                     int64_t *cta_tile_begin, int64_t *seg_tile_begin) {
+    g_last_error.clear();
+    if (!seqlens || !N_out || !P_out) return fail(ATTN_ERR_NULL, "seqlens, N_out and P_out must be non-NULL");
+    if (B <= 0 || KH <= 0) return fail(ATTN_ERR_SHAPE, "B and KH must be positive");
+    if (B > ATTN_MAX_BATCH) return fail(ATTN_ERR_UNSUPPORTED, "B=%d exceeds %d", B, ATTN_MAX_BATCH);
+    if (tile_keys <= 0 || num_ctas <= 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be positive");
+    LeanPlan plan;
+    int st = build_plan(seqlens, B, KH, tile_keys, -1, &plan);
+    if (st != ATTN_OK) return st;
+    int P = num_ctas;
+    if (plan.N > 0 && P > plan.N) P = (int)plan.N;
+    plan.P = P;
+    *N_out = plan.N;
+    *P_out = P;
+    if (cta_tile_begin)
+        for (int c = 0; c <= P; ++c) cta_tile_begin[c] = plan.N > 0 ? plan_cta_begin(plan, c) : 0;
+    if (seg_tile_begin) {
+        for (int b = 0; b < B; ++b) {
+            const int nb = plan_tiles_per_segment(plan, b);
+            for (int kh = 0; kh < KH; ++kh) seg_tile_begin[b * KH + kh] = plan.tile_prefix[b] + (int64_t)kh * nb;
+        }
+        seg_tile_begin[B * KH] = plan.N;
+    }
+    return ATTN_OK;
+}
+
+int attn_prefill_causal(const void *q, const void *k, const void *v, int B, int ISL, int Hq, int KH, int Hsz,
+                        void *out, hipStream_t stream) {
+    g_last_error.clear();
+    if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+    if (B <= 0 || ISL < 0 || Hq <= 0 || KH <= 0)
+        return fail(ATTN_ERR_SHAPE, "B, Hq, KH must be positive and ISL non-negative");
+    if (Hq % KH != 0) return fail(ATTN_ERR_SHAPE, "Hq=%d is not a multiple of KH=%d", Hq, KH);
+    if (Hsz != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill supports Hsz=128 (got %d)", Hsz);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(ATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+    if (ISL == 0) return ATTN_OK;
+    const float scale_log2 = (1.0f / sqrtf((float)Hsz)) * 1.4426950408889634f;
+    hipError_t e = attn::launch_prefill_causal(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                               static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out), B,
+                                               ISL, Hq, KH, Hsz, scale_log2, stream);
+    if (e != hipSuccess) return fail_hip(e, "prefill kernel launch");
+    return ATTN_OK;
+}
+
+int attn_hbm_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (!src || !dst) return fail(ATTN_ERR_NULL, "src and dst must be non-NULL");
+    if (bytes % 16 != 0) return fail(ATTN_ERR_SHAPE, "bytes=%zu is not a multiple of 16", bytes);
+    if (!aligned16(src) || !aligned16(dst)) return fail(ATTN_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    hipError_t e = attn::launch_copy_probe(src, dst, bytes, stream);
+    if (e != hipSuccess) return fail_hip(e, "copy probe launch");
+    return ATTN_OK;
+}
+
+int attn_device_info(int *num_cus, int *lds_bytes_per_cu) {
+    g_last_error.clear();
+    if (!num_cus || !lds_bytes_per_cu) return fail(ATTN_ERR_NULL, "outputs must be non-NULL");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    e = hipDeviceGetAttribute(lds_bytes_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(MaxSharedMemoryPerMultiprocessor)");
+    return ATTN_OK;
+}
+
+int attn_release(void) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    int st = ATTN_OK;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        if ((e = hipSetDevice(kv.first.first)) == hipSuccess) e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        if (e != hipSuccess) st = fail_hip(e, "releasing workspace");
+        kv.second = Workspace();
+    }
+    g_ws.clear();
+    (void)hipSetDevice(cur);
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// common.h -- types and launcher declarations shared by the HIP sources of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxGroup = 16;       // query heads per kv head held by one workgroup (MFMA N = 16)
+constexpr int kDecodeWaves = 8;     // waves per decode workgroup
+constexpr int kKeysPerBlock = 32;   // keys one wave consumes per step (two 16-key MFMA row blocks)
+constexpr int kDefaultTileKeys = kDecodeWaves * kKeysPerBlock;  // one block per wave per LeanTile
+
+// Kernel arguments of the decode tile kernel (passed by value: the plan rides in kernargs).
+struct DecodeParams {
+    const uint16_t *q;   // bf16 [B][Hq][Hsz]
+    const uint16_t *k;   // bf16 [B][KH][S][Hsz]
+    const uint16_t *v;   // bf16 [B][KH][S][Hsz]
+    float *out;          // fp32 [B][Hq][Hsz]
+    float *ws;           // partial slots, each slot_floats long
+    int64_t kv_stride;   // S
+    int Hq;
+    int G;
+    int slot_floats;     // G*Hsz (O) + G (m) + G (l), rounded up to a multiple of 4
+    float scale_log2;    // softmax scale * log2(e)
+    LeanPlan plan;
+};
+
+// Partial slot layout: O[G][Hsz] unnormalised, then m[G] (log2 domain), then l[G].
+inline int decode_slot_floats(int G, int Hsz) { return (G * Hsz + 2 * G + 3) & ~3; }
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams &p, int Hsz, hipStream_t stream);
+int decode_tiles_occupancy(int Hsz, int G);  // resident decode workgroups per CU
+hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
+                                 int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
+                                 hipStream_t stream);
+hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+}  // namespace attn

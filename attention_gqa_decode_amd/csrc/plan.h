@@ -1,0 +1,96 @@
+// plan.h -- the LeanTile work split, shared by the host planner and the kernels.
+//
+// Source: "LeanAttention" digest (siliconandsystems.com), sections "조각별로 합칠
+// 수 있는 정확한 소프트맥스" (a global work id maps tiles of (batch, head,
+// context range) to CTAs, stream-K style) and "하드웨어에 맞춘 작업 단위" (tile
+// count follows from the total work and the number of compute units; resident
+// CTAs take the next tile instead of a fixed split).
+//
+// Numbering.  Segment s = b*KH + kh is the context of request b under kv head
+// kh; it holds n_b = ceil(L_b / T) LeanTiles of T keys.  Tiles are numbered in
+// segment order: batch b owns tiles [tile_prefix[b], tile_prefix[b+1]) with
+// tile_prefix[b+1] - tile_prefix[b] = KH * n_b, and within the batch kv head
+// kh owns the kh-th run of n_b tiles.  With N tiles and P CTAs, CTA c owns
+// [floor(cN/P), floor((c+1)N/P)); the planner keeps P <= N so no CTA is empty
+// and the loads of any two CTAs differ by at most one tile.
+//
+// Pieces and partial slots.  The part of a segment inside one CTA's range is
+// a piece.  A piece that is the whole segment is finished by its CTA.  Only a
+// CTA's first and last pieces can be partial, so each CTA c owns two partial
+// slots: 2c for its first piece and 2c+1 for its last piece.  A segment whose
+// tiles span CTAs c_lo..c_hi (c_lo < c_hi) leaves one partial in each of them:
+// CTA c_lo's slot is 2*c_lo if the segment starts exactly where c_lo's range
+// starts (then it is c_lo's first piece) and 2*c_lo+1 otherwise; every later
+// CTA holds the segment as its first piece, slot 2c.
+#pragma once
+
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define ATTN_HD __host__ __device__ inline
+#else
+#define ATTN_HD inline
+#endif
+
+#ifndef ATTN_MAX_BATCH
+#define ATTN_MAX_BATCH 256
+#endif
+
+struct LeanPlan {
+    int B;
+    int KH;
+    int T;      // keys per LeanTile
+    int P;      // CTAs (1 <= P <= N when N > 0)
+    int64_t N;  // total tiles
+    int32_t seqlen[ATTN_MAX_BATCH];           // L_b
+    int32_t tile_prefix[ATTN_MAX_BATCH + 1];  // tiles before batch b (all its kv heads)
+};
+
+ATTN_HD int64_t plan_cta_begin(const LeanPlan &p, int c) { return (int64_t)c * p.N / p.P; }
+
+// CTA whose range contains tile t: the largest c with floor(cN/P) <= t.
+ATTN_HD int plan_cta_of_tile(const LeanPlan &p, int64_t t) { return (int)(((t + 1) * p.P - 1) / p.N); }
+
+ATTN_HD int plan_tiles_per_segment(const LeanPlan &p, int b) {
+    return (p.tile_prefix[b + 1] - p.tile_prefix[b]) / p.KH;
+}
+
+// Batch owning tile t (0 <= t < N): the b with tile_prefix[b] <= t < tile_prefix[b+1].
+ATTN_HD int plan_batch_of_tile(const LeanPlan &p, int64_t t) {
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (p.tile_prefix[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+struct LeanPiece {
+    int b, kh;
+    int64_t seg_begin, seg_end;    // tiles of the whole segment
+    int64_t tile_begin, tile_end;  // tiles of this piece
+    int key_begin, key_end;        // keys of this piece, 0 <= key_begin < key_end <= L_b
+};
+
+// The piece that starts at tile t inside a CTA range ending at cta_end.
+ATTN_HD LeanPiece plan_piece_at(const LeanPlan &p, int64_t t, int64_t cta_end) {
+    LeanPiece pc;
+    pc.b = plan_batch_of_tile(p, t);
+    int nb = plan_tiles_per_segment(p, pc.b);
+    int64_t local = t - p.tile_prefix[pc.b];
+    pc.kh = (int)(local / nb);
+    pc.seg_begin = p.tile_prefix[pc.b] + (int64_t)pc.kh * nb;
+    pc.seg_end = pc.seg_begin + nb;
+    pc.tile_begin = t;
+    pc.tile_end = pc.seg_end < cta_end ? pc.seg_end : cta_end;
+    int L = p.seqlen[pc.b];
+    pc.key_begin = (int)((pc.tile_begin - pc.seg_begin) * p.T);
+    int64_t ke = (pc.tile_end - pc.seg_begin) * (int64_t)p.T;
+    pc.key_end = ke < L ? (int)ke : L;
+    return pc;
+}
+
+// Partial slot of CTA c's piece in a split segment that starts at tile seg_begin.
+ATTN_HD int plan_slot(const LeanPlan &p, int c, int64_t seg_begin) {
+    return 2 * c + (seg_begin <= plan_cta_begin(p, c) ? 0 : 1);
+}

@@ -1,0 +1,172 @@
+/*
+ * attn_gqa.h -- C ABI of the MI355X (gfx950) grouped-query attention library.
+ *
+ * The library computes exact softmax attention forward for grouped-query
+ * attention (GQA): G = Hq / KH query heads share one K/V head, query head h
+ * reads K/V head h / G (contiguous groups).  Sources, cited by page title and
+ * section heading:
+ *   - "장문 컨텍스트 추론을 위한 어텐션 공동 설계" (aitrends.kr, attention
+ *     co-design), sections "프리필과 디코드의 차이" (decode reads the KV cache
+ *     from HBM and is memory bound; prefill is a large matmul), "FlashAttention과
+ *     GEMM 모양" (fused QK^T -> online softmax (running max and sum) -> PV over
+ *     streamed K/V tiles) and "그룹 크기(G)의 영향";
+ *   - "필수 LLM 최적화 기법(2)" (synabreu.github.io), section 1-1 (MHA, MQA,
+ *     GQA; Llama-3 uses 32 query heads over 8 K/V heads);
+ *   - "LeanAttention" digest (siliconandsystems.com), sections "조각별로 합칠 수
+ *     있는 정확한 소프트맥스" (partial (max, sum, weighted V) states merged by
+ *     rescaling to the common max) and "하드웨어에 맞춘 작업 단위" (tile count
+ *     from total work and compute-unit count; resident CTAs take the next tile).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     memory) unless the argument says "host".  The caller owns every tensor;
+ *     the library never frees caller memory.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (the
+ *     bfloat16 storage format); tensors are dense and row-major in the stated
+ *     dimension order.  Tensor pointers must be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  Argument
+ *     errors are detected and returned synchronously before anything is
+ *     enqueued; the call then has no effect.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code.  A readable
+ *     message for the most recent failure on the calling thread is available
+ *     from attn_last_error().  No C++ exception crosses this interface.
+ *   - Numerics: bf16 inputs, fp32 accumulation; the softmax is evaluated with
+ *     exp2 and the scale multiplied by log2(e).  Results do not depend on the
+ *     work split beyond fp32 rounding.  NaN/Inf inputs are outside the contract.
+ */
+#ifndef ATTN_GQA_H
+#define ATTN_GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,       /* inconsistent sizes (B <= 0, Hq % KH != 0, L_b < 0 or > stride, ...) */
+    ATTN_ERR_UNSUPPORTED = -3, /* valid but not implemented (Hsz not in {64,128,256}, G > 16, B > 256, ...) */
+    ATTN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = -5,   /* caller workspace too small */
+    ATTN_ERR_HIP = -6          /* a HIP runtime call failed; see attn_last_error() */
+};
+
+/* Largest batch the decode planner accepts (its plan travels in kernel arguments). */
+#define ATTN_MAX_BATCH 256
+/* Largest group size G = Hq / KH the decode kernel holds in one workgroup. */
+#define ATTN_MAX_GROUP 16
+
+/*
+ * attn_decode -- one decode step of GQA attention (query length 1).
+ *
+ *   q        bf16 [B][Hq][Hsz]          query of the new token of each request
+ *   k_cache  bf16 [B][KH][S][Hsz]       keys; request b uses rows 0..L_b-1
+ *   v_cache  bf16 [B][KH][S][Hsz]       values, same layout
+ *   seqlens  HOST int32 [B]             L_b, context length of request b
+ *                                       (0 <= L_b; L_b = 0 yields a zero row)
+ *   out      fp32 [B][Hq][Hsz]          softmax(q k^T / sqrt(Hsz)) v per head
+ *   S (the cache capacity per (b, kv head)) is max_b L_b: the cache is packed
+ *   to the longest request.  Use attn_decode_ex for any other capacity.
+ *
+ * The context of every (request, kv head) is cut into LeanTiles of T keys; the
+ * tiles of the whole batch are numbered globally and split evenly over all
+ * resident workgroups, each of which keeps the G query heads of a group
+ * together.  Heads split across workgroups leave partial (max, sum, O) states
+ * that a second kernel merges.  The library owns the partial-state buffer
+ * (one per device and stream, grown on demand with hipMalloc, freed by
+ * attn_release); calls on the same stream are ordered, calls that share a
+ * stream from several host threads at once are not supported.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
+                int B, int Hq, int KH, int Hsz, float *out, hipStream_t stream);
+
+/* Full-control decode.  Fields not listed keep the attn_decode meaning. */
+typedef struct attn_decode_args {
+    const void *q;            /* bf16 [B][Hq][Hsz] */
+    const void *k_cache;      /* bf16 [B][KH][kv_stride][Hsz] */
+    const void *v_cache;      /* bf16 [B][KH][kv_stride][Hsz] */
+    const int32_t *seqlens;   /* HOST int32 [B], 0 <= L_b <= kv_stride */
+    float *out;               /* fp32 [B][Hq][Hsz] */
+    int B, Hq, KH, Hsz;
+    int64_t kv_stride;        /* cache capacity S per (b, kv head); 0 = max_b L_b */
+    float scale;              /* softmax scale; <= 0 selects 1/sqrt(Hsz) */
+    void *workspace;          /* optional device buffer for partial states (NULL = library-owned) */
+    size_t workspace_bytes;   /* its size; must be >= attn_decode_workspace_bytes(...) */
+    int tile_keys;            /* LeanTile size T in keys; 0 = library default */
+    int num_ctas;             /* number of persistent workgroups P; 0 = all resident slots */
+    hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the tile kernel */
+    hipEvent_t ev_tiles_end;  /* optional: recorded right after the tile kernel */
+} attn_decode_args;
+
+int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
+
+/*
+ * Bytes of partial-state workspace attn_decode_ex needs for these sizes when
+ * it runs with `num_ctas` workgroups (0 = the library's default for the
+ * current device; that query initialises the HIP runtime).  Returns 0 for
+ * unsupported sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas);
+
+/*
+ * attn_prefill_causal -- causal GQA attention over a whole prompt.
+ *
+ *   q    bf16 [B][Hq][ISL][Hsz]
+ *   k    bf16 [B][KH][ISL][Hsz]   (the decode cache layout, capacity ISL)
+ *   v    bf16 [B][KH][ISL][Hsz]
+ *   out  bf16 [B][Hq][ISL][Hsz]   row i = softmax over keys 0..i (top-left
+ *                                 causal mask), scale 1/sqrt(Hsz), fp32
+ *                                 accumulation, rounded to bf16 once at the end
+ * QK^T runs on bf16 MFMA; the PV product runs on fp16 MFMA with V converted
+ * bf16 -> fp16 (exact for |v| < 65504; larger |v| is outside the contract) and
+ * the softmax weights rounded to fp16.
+ * Source: co-design page, sections "프리필과 디코드의 차이" and "FlashAttention과
+ * GEMM 모양" (prefill is the large, compute-bound matmul form of the same
+ * fused kernel).  Hsz must be 128 in this version.
+ */
+int attn_prefill_causal(const void *q, const void *k, const void *v, int B, int ISL, int Hq, int KH,
+                        int Hsz, void *out, hipStream_t stream);
+
+/*
+ * attn_decode_plan -- the host half of the LeanTile planner, exposed for
+ * inspection (no GPU use).  For the given HOST seqlens it returns the number
+ * of tiles N and, if the arrays are non-NULL:
+ *   cta_tile_begin  int64 [P+1]   CTA c owns global tiles [begin[c], begin[c+1])
+ *   seg_tile_begin  int64 [B*KH+1] segment s = b*KH + kh owns tiles
+ *                                  [seg_tile_begin[s], seg_tile_begin[s+1])
+ * `num_ctas` must be > 0 here; the effective P is min(num_ctas, N) and is
+ * written to *P_out.
+ */
+int attn_decode_plan(const int32_t *seqlens, int B, int KH, int tile_keys, int num_ctas,
+                     int64_t *N_out, int *P_out, int64_t *cta_tile_begin, int64_t *seg_tile_begin);
+
+/*
+ * attn_hbm_copy_probe -- plain device-to-device copy of `bytes` (a multiple of
+ * 16) from src to dst with 16-byte vector loads and stores.  A measurement
+ * reference of known traffic: it calibrates the HBM byte counters and gives
+ * the practical streaming ceiling next to the 8 TB/s peak.
+ */
+int attn_hbm_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+/* Compute units and LDS bytes per compute unit of the current device. */
+int attn_device_info(int *num_cus, int *lds_bytes_per_cu);
+
+/* Frees every library-owned workspace on every device (synchronises them). */
+int attn_release(void);
+
+/* Static description of a status code. */
+const char *attn_status_string(int status);
+
+/* Message for the most recent failure on the calling thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GQA_H */

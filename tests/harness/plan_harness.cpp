@@ -1,0 +1,70 @@
+// Host-only harness over the LeanTile plan header the kernels use.  It walks
+// every CTA's tile range exactly as the decode tile kernel does and lists, for
+// every segment, the partial slots the merge kernel would read.  Built with g++
+// by tests/test_plan.py; no GPU involved.
+#include <stdint.h>
+
+#include "../../attention_gqa_decode_amd/csrc/plan.h"
+
+extern "C" {
+
+// rows of 8 int64: cta, b, kh, tile_begin, tile_end, key_begin, key_end, slot (-1 = whole segment)
+int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int64_t *rows, int64_t max_rows) {
+    LeanPlan p;
+    p.B = B;
+    p.KH = KH;
+    p.T = T;
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        p.seqlen[b] = seqlens[b];
+        p.tile_prefix[b] = (int32_t)acc;
+        acc += (int64_t)KH * ((seqlens[b] + (int64_t)T - 1) / T);
+    }
+    p.tile_prefix[B] = (int32_t)acc;
+    p.N = acc;
+    p.P = P;
+    int64_t n = 0;
+    for (int c = 0; c < P; ++c) {
+        int64_t t = plan_cta_begin(p, c), te = plan_cta_begin(p, c + 1);
+        while (t < te) {
+            LeanPiece pc = plan_piece_at(p, t, te);
+            bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
+            if (n < max_rows) {
+                int64_t *r = rows + 8 * n;
+                r[0] = c; r[1] = pc.b; r[2] = pc.kh; r[3] = pc.tile_begin; r[4] = pc.tile_end;
+                r[5] = pc.key_begin; r[6] = pc.key_end; r[7] = whole ? -1 : plan_slot(p, c, pc.seg_begin);
+            }
+            ++n;
+            t = pc.tile_end;
+        }
+    }
+    return n;
+}
+
+// For segment s = b*KH + kh: writes the slots the merge kernel reads, returns their count
+// (0 when the segment is finished by one CTA or is empty).
+int harness_merge_slots(const int32_t *seqlens, int B, int KH, int T, int P, int s, int32_t *slots, int max_slots) {
+    LeanPlan p;
+    p.B = B;
+    p.KH = KH;
+    p.T = T;
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        p.seqlen[b] = seqlens[b];
+        p.tile_prefix[b] = (int32_t)acc;
+        acc += (int64_t)KH * ((seqlens[b] + (int64_t)T - 1) / T);
+    }
+    p.tile_prefix[B] = (int32_t)acc;
+    p.N = acc;
+    p.P = P;
+    int b = s / KH, kh = s % KH;
+    int nb = plan_tiles_per_segment(p, b);
+    if (nb == 0) return 0;
+    int64_t seg_begin = p.tile_prefix[b] + (int64_t)kh * nb;
+    int c_lo = plan_cta_of_tile(p, seg_begin), c_hi = plan_cta_of_tile(p, seg_begin + nb - 1);
+    if (c_lo == c_hi) return 0;
+    int k = c_hi - c_lo + 1;
+    for (int i = 0; i < k && i < max_slots; ++i) slots[i] = i == 0 ? plan_slot(p, c_lo, seg_begin) : 2 * (c_lo + i);
+    return k;
+}
+}

@@ -1,0 +1,154 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments synchronously (before any HIP call, so these run without a GPU).
+
+Only argument combinations that fail validation are passed; the fake device addresses
+below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_gqa_decode_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_gqa.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["attn_decode", "attn_decode_ex", "attn_decode_workspace_bytes", "attn_prefill_causal",
+              "attn_decode_plan", "attn_hbm_copy_probe", "attn_device_info", "attn_release",
+              "attn_status_string", "attn_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_no_oracle_symbols_in_library():
+    lib = A.lib()
+    for n in ["oracle_decode_f64", "oracle_prefill_causal_f64", "oracle_bf16_to_f64"]:
+        assert not hasattr(lib, n)
+
+
+def test_status_strings():
+    lib = A.lib()
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        assert lib.attn_status_string(code).decode() not in ("", "unknown status")
+    assert lib.attn_status_string(-99).decode() == "unknown status"
+
+
+def call_decode(q=FAKE, k=FAKE, v=FAKE, sl=(4, 4), B=2, Hq=8, KH=2, Hsz=128, out=FAKE):
+    lib = A.lib()
+    arr = None if sl is None else np.ascontiguousarray(sl, dtype=np.int32)
+    return lib.attn_decode(q, k, v, None if arr is None else arr.ctypes.data, B, Hq, KH, Hsz, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), A.ATTN_ERR_NULL),
+    (dict(k=None), A.ATTN_ERR_NULL),
+    (dict(v=None), A.ATTN_ERR_NULL),
+    (dict(out=None), A.ATTN_ERR_NULL),
+    (dict(sl=None), A.ATTN_ERR_NULL),
+    (dict(B=0, sl=(4,)), A.ATTN_ERR_SHAPE),
+    (dict(Hq=6, KH=4), A.ATTN_ERR_SHAPE),
+    (dict(KH=0), A.ATTN_ERR_SHAPE),
+    (dict(Hsz=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hsz=512), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=64, KH=2), A.ATTN_ERR_UNSUPPORTED),
+    (dict(B=257, sl=(1,) * 257), A.ATTN_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), A.ATTN_ERR_ALIGN),
+    (dict(out=FAKE + 4), A.ATTN_ERR_ALIGN),
+    (dict(v=FAKE + 8), A.ATTN_ERR_ALIGN),
+    (dict(sl=(4, -1)), A.ATTN_ERR_SHAPE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert call_decode(**kw) == status
+    assert A.lib().attn_last_error().decode() != ""
+
+
+def ex_args(**kw):
+    a = A.attn_decode_args()
+    sl = np.ascontiguousarray(kw.pop("seqlens", (4, 4)), dtype=np.int32)
+    a.q = a.k_cache = a.v_cache = a.out = FAKE
+    a.seqlens = sl.ctypes.data
+    a.B, a.Hq, a.KH, a.Hsz = 2, 8, 2, 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a, sl
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_stride=3), A.ATTN_ERR_SHAPE),           # L_b = 4 > stride
+    (dict(kv_stride=-1), A.ATTN_ERR_SHAPE),
+    (dict(tile_keys=-5), A.ATTN_ERR_SHAPE),
+    (dict(num_ctas=-1), A.ATTN_ERR_SHAPE),
+    (dict(scale=float("inf")), A.ATTN_ERR_SHAPE),
+    (dict(scale=float("nan")), A.ATTN_ERR_SHAPE),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 20), A.ATTN_ERR_ALIGN),
+    (dict(workspace=FAKE, workspace_bytes=16, num_ctas=4), A.ATTN_ERR_WORKSPACE),
+])
+def test_decode_ex_rejects_bad_arguments(kw, status):
+    a, _sl = ex_args(**kw)
+    assert A.lib().attn_decode_ex(ctypes.byref(a), None) == status
+
+
+def test_decode_ex_null_args():
+    assert A.lib().attn_decode_ex(None, None) == A.ATTN_ERR_NULL
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE, 1, 16, 8, 2, 128, FAKE), A.ATTN_ERR_NULL),
+    ((FAKE, FAKE, FAKE, 0, 16, 8, 2, 128, FAKE), A.ATTN_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, 1, -1, 8, 2, 128, FAKE), A.ATTN_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 16, 8, 3, 128, FAKE), A.ATTN_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 16, 8, 2, 64, FAKE), A.ATTN_ERR_UNSUPPORTED),
+    ((FAKE + 2, FAKE, FAKE, 1, 16, 8, 2, 128, FAKE), A.ATTN_ERR_ALIGN),
+    ((FAKE, FAKE, FAKE, 1, 0, 8, 2, 128, FAKE), A.ATTN_OK),  # empty prompt: nothing to do, no launch
+])
+def test_prefill_argument_checks(args, status):
+    assert A.lib().attn_prefill_causal(*args, None) == status
+
+
+def test_copy_probe_argument_checks():
+    lib = A.lib()
+    assert lib.attn_hbm_copy_probe(None, FAKE, 64, None) == A.ATTN_ERR_NULL
+    assert lib.attn_hbm_copy_probe(FAKE, FAKE, 65, None) == A.ATTN_ERR_SHAPE
+    assert lib.attn_hbm_copy_probe(FAKE + 8, FAKE, 64, None) == A.ATTN_ERR_ALIGN
+
+
+def test_plan_argument_checks():
+    with pytest.raises(A.AttnError) as e:
+        A.attn_decode_plan([4, 4], 2, 0, 4)
+    assert e.value.status == A.ATTN_ERR_SHAPE
+    with pytest.raises(A.AttnError) as e:
+        A.attn_decode_plan([4, -4], 2, 16, 4)
+    assert e.value.status == A.ATTN_ERR_SHAPE
+
+
+def test_workspace_bytes_formula():
+    # 2 slots per CTA, each G*Hsz (O) + 2G (m, l) floats rounded up to 4
+    assert A.attn_decode_workspace_bytes(16, 32, 8, 128, 100) == 2 * 100 * ((4 * 128 + 8 + 3) & ~3) * 4
+    assert A.attn_decode_workspace_bytes(1, 8, 1, 64, 7) == 2 * 7 * ((8 * 64 + 16 + 3) & ~3) * 4
+    assert A.attn_decode_workspace_bytes(1, 8, 3, 64, 7) == 0  # Hq % KH != 0
+
+
+def test_python_binding_validates_cache_capacity():
+    import torch
+    # CPU tensors are rejected before anything reaches the library
+    with pytest.raises(TypeError):
+        A.attn_decode(torch.zeros(1, 8, 128, dtype=torch.bfloat16), torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16),
+                      torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16), [4])

@@ -1,0 +1,126 @@
+"""CPU tests of the LeanTile planner (host export and the shared plan header).
+
+The work split follows the LeanAttention digest, sections "조각별로 합칠 수 있는 정확한
+소프트맥스" (global tile ids over (batch, head, context range), stream-K style) and
+"하드웨어에 맞춘 작업 단위" (tile count from total work and unit count).  Properties:
+every key of every (request, kv head) is covered exactly once, CTA loads differ by at
+most one tile, only a CTA's first and last pieces are partial, every partial slot is
+written once, and the merge reads exactly the slots the tile kernel wrote.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def harness(tmp_path_factory):
+    out = tmp_path_factory.mktemp("plan") / "libplan_harness.so"
+    src = os.path.join(ROOT, "tests", "harness", "plan_harness.cpp")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-Wall", "-Werror", "-o", str(out), src],
+                   check=True)
+    lib = ctypes.CDLL(str(out))
+    lib.harness_pieces.restype = ctypes.c_int64
+    lib.harness_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_int64]
+    lib.harness_merge_slots.restype = ctypes.c_int
+    lib.harness_merge_slots.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    return lib
+
+
+def pieces(harness, sl, KH, T, P):
+    sl = np.ascontiguousarray(sl, dtype=np.int32)
+    n = harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, None, 0)
+    rows = np.zeros((max(n, 1), 8), dtype=np.int64)
+    harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, rows.ctypes.data, n)
+    return rows[:n]
+
+
+def merge_slots(harness, sl, KH, T, P, s):
+    sl = np.ascontiguousarray(sl, dtype=np.int32)
+    buf = np.zeros(4 * P + 4, dtype=np.int32)
+    k = harness.harness_merge_slots(sl.ctypes.data, len(sl), KH, T, P, s, buf.ctypes.data, len(buf))
+    return buf[:k].tolist()
+
+
+def total_tiles(sl, KH, T):
+    return sum(KH * ((L + T - 1) // T) for L in sl)
+
+
+CASES = [
+    ([1024], 2, 256, 8),
+    ([8192] * 16, 8, 256, 256),
+    ([262144], 1, 256, 256),
+    ([262144], 1, 16, 1000),
+    ([0, 1, 5, 0, 300, 17], 3, 16, 7),
+    ([518, 64654, 3000, 777], 8, 100, 13),
+    ([1], 1, 1, 1),
+    ([33, 31, 0], 2, 1024, 3),
+]
+
+
+@pytest.mark.parametrize("sl,KH,T,P", CASES)
+def test_every_key_covered_once_and_slots_consistent(harness, sl, KH, T, P):
+    N = total_tiles(sl, KH, T)
+    P = min(P, N) if N else 1
+    rows = pieces(harness, sl, KH, T, P)
+    cover = {}
+    per_cta_tiles = np.zeros(P, dtype=np.int64)
+    written = {}
+    for c, b, kh, tb, te, kb, ke, slot in rows:
+        assert 0 <= kb < ke <= sl[b]
+        cover.setdefault((b, kh), []).append((kb, ke))
+        per_cta_tiles[c] += te - tb
+        if slot >= 0:
+            assert slot in (2 * c, 2 * c + 1)
+            assert slot not in written, "partial slot written twice"
+            written[slot] = (b, kh)
+    for b, L in enumerate(sl):
+        for kh in range(KH):
+            segs = sorted(cover.get((b, kh), []))
+            if L == 0:
+                assert not segs
+                continue
+            assert segs[0][0] == 0 and segs[-1][1] == L
+            for (a0, a1), (b0, b1) in zip(segs, segs[1:]):
+                assert a1 == b0, "gap or overlap between pieces"
+            expect = merge_slots(harness, sl, KH, T, P, b * KH + kh)
+            got = sorted(s for s, seg in written.items() if seg == (b, kh))
+            if len(segs) == 1:
+                assert expect == [] and got == []
+            else:
+                assert sorted(expect) == got
+    if N:
+        assert per_cta_tiles.max() - per_cta_tiles.min() <= 1
+        assert per_cta_tiles.sum() == N
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_plans(harness, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    KH = int(rng.integers(1, 9))
+    sl = rng.integers(0, 5000, B)
+    sl[rng.random(B) < 0.2] = 0
+    T = int(rng.choice([1, 16, 32, 48, 100, 256, 1024]))
+    P = int(rng.integers(1, 600))
+    test_every_key_covered_once_and_slots_consistent(harness, sl.tolist(), KH, T, P)
+
+
+def test_library_planner_matches_header(harness):
+    import attention_gqa_decode_amd as A
+    sl = [518, 64654, 3000, 0, 777]
+    N, P, cta, seg = A.attn_decode_plan(sl, 8, 100, 13)
+    assert N == total_tiles(sl, 8, 100) and P == 13
+    assert cta[0] == 0 and cta[-1] == N and np.all(np.diff(cta) >= 1)
+    assert np.all(np.diff(cta) - np.diff(cta).min() <= 1)
+    assert seg[-1] == N and np.all(np.diff(seg) >= 0)
+    rows = pieces(harness, sl, 8, 100, 13)
+    for c in range(P):
+        mine = rows[rows[:, 0] == c]
+        assert mine[0, 3] == cta[c] and mine[-1, 4] == cta[c + 1]

@@ -1,0 +1,72 @@
+"""GPU parity of causal prefill against the fp64 oracle.
+
+The output is bf16, so the bar is |gpu - oracle| <= 2e-3 + half a bf16 ulp of the oracle
+value (the rounding of the output alone can reach half an ulp).  Small prompts are
+checked on every row; the full 8192-token workload on its first and last rows plus a
+seeded sample.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_gqa_decode_amd as A
+import oracle
+from attention_gqa_decode_amd import workloads as W
+from attention_gqa_decode_amd.workloads import bits
+from gpu_util import bf16_half_ulp, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_and_check(B, ISL, Hq, KH, Hsz, seed, rows=None):
+    s = W.PrefillShape("t", B, ISL, Hq, KH, Hsz, seed=seed)
+    q, k, v = W.prefill_inputs(s, device="cuda")
+    out = A.attn_prefill_causal(q, k, v)
+    torch.cuda.synchronize()
+    got = out.float().cpu().double().numpy().reshape(-1, Hsz)
+    ref = oracle.prefill_causal(bits(q), bits(k), bits(v), KH, 1 / math.sqrt(Hsz), rows=rows).reshape(-1, Hsz)
+    sel = np.arange(got.shape[0]) if rows is None else np.asarray(rows)
+    g, r = got[sel], ref[sel]
+    assert np.all(np.isfinite(g))
+    excess = np.abs(g - r) - (2e-3 + bf16_half_ulp(r))
+    note(f"  max |err| {np.abs(g - r).max():.3e}, worst excess over bound {excess.max():.3e}")
+    assert excess.max() <= 0, f"max |err| {np.abs(g - r).max():.3e}"
+
+
+@pytest.mark.parametrize("ISL", [1, 5, 64, 128, 129, 300])
+def test_small_prompts(ISL):
+    note(f"prefill B=2 ISL={ISL} Hq=8 KH=2")
+    run_and_check(2, ISL, 8, 2, 128, seed=ISL)
+
+
+@pytest.mark.parametrize("Hq,KH", [(4, 1), (8, 8), (16, 2)])
+def test_group_sizes(Hq, KH):
+    note(f"prefill ISL=1000 Hq={Hq} KH={KH}")
+    run_and_check(1, 1000, Hq, KH, 128, seed=Hq * 10 + KH)
+
+
+def test_row0_is_v0():
+    s = W.PrefillShape("t", 1, 256, 8, 2, 128, seed=3)
+    q, k, v = W.prefill_inputs(s, device="cuda")
+    out = A.attn_prefill_causal(q, k, v)
+    torch.cuda.synchronize()
+    for h in range(8):
+        assert torch.equal(out[0, h, 0], v[0, h // 4, 0])
+
+
+def test_full_size_sampled_rows():
+    s = W.prefill_workload()
+    note(f"prefill full-size B={s.B} ISL={s.ISL} Hq={s.Hq} KH={s.KH}")
+    rng = np.random.default_rng(5)
+    heads = [0, 5, 17, 31]
+    picks = list(range(0, 64)) + list(range(s.ISL - 64, s.ISL)) + rng.choice(s.ISL, 64, replace=False).tolist()
+    rows = np.array([h * s.ISL + i for h in heads for i in picks])
+    run_and_check(s.B, s.ISL, s.Hq, s.KH, s.Hsz, seed=s.seed, rows=rows)
