@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_plan.restype = _I
     L.attn_hbm_copy_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
     L.attn_hbm_copy_probe.restype = _I
+    L.attn_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+    L.attn_hbm_read_probe.restype = _I
     L.attn_device_info.argtypes = [_P, _P]
     L.attn_device_info.restype = _I
     L.attn_release.argtypes = []
@@ -204,6 +206,11 @@ def attn_decode_plan(seqlens, KH: int, tile_keys: int, num_ctas: int):
 def attn_hbm_copy_probe(src, dst, nbytes=None, stream=None):
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(lib().attn_hbm_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream)))
+
+
+def attn_hbm_read_probe(src, sink, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().attn_hbm_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), _stream_handle(stream)))
 
 
 def attn_device_info():

@@ -186,7 +186,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (stride == 0) {
         for (int b = 0; b < a->B; ++b) stride = a->seqlens[b] > stride ? a->seqlens[b] : stride;
     }
-    const int T = a->tile_keys > 0 ? a->tile_keys : attn::kDefaultTileKeys;
+    const int T = a->tile_keys > 0 ? a->tile_keys : attn::decode_tile_keys(a->Hsz);
 
     attn::DecodeParams p;
     st = build_plan(a->seqlens, a->B, a->KH, T, stride, &p.plan);
@@ -315,6 +315,16 @@ int attn_hbm_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t st
     if (!aligned16(src) || !aligned16(dst)) return fail(ATTN_ERR_ALIGN, "src and dst must be 16-byte aligned");
     hipError_t e = attn::launch_copy_probe(src, dst, bytes, stream);
     if (e != hipSuccess) return fail_hip(e, "copy probe launch");
+    return ATTN_OK;
+}
+
+int attn_hbm_read_probe(const void *src, size_t bytes, void *sink, hipStream_t stream) {
+    g_last_error.clear();
+    if (!src || !sink) return fail(ATTN_ERR_NULL, "src and sink must be non-NULL");
+    if (bytes % 16 != 0) return fail(ATTN_ERR_SHAPE, "bytes=%zu is not a multiple of 16", bytes);
+    if (!aligned16(src) || !aligned16(sink)) return fail(ATTN_ERR_ALIGN, "src and sink must be 16-byte aligned");
+    hipError_t e = attn::launch_read_probe(src, bytes, sink, stream);
+    if (e != hipSuccess) return fail_hip(e, "read probe launch");
     return ATTN_OK;
 }
 

@@ -14,9 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGroup = 16;       // query heads per kv head held by one workgroup (MFMA N = 16)
-constexpr int kDecodeWaves = 8;     // waves per decode workgroup
 constexpr int kKeysPerBlock = 32;   // keys one wave consumes per step (two 16-key MFMA row blocks)
-constexpr int kDefaultTileKeys = kDecodeWaves * kKeysPerBlock;  // one block per wave per LeanTile
 
 // Kernel arguments of the decode tile kernel (passed by value: the plan rides in kernargs).
 struct DecodeParams {
@@ -40,9 +38,11 @@ inline int decode_slot_floats(int G, int Hsz) { return (G * Hsz + 2 * G + 3) & ~
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &p, int Hsz, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int G);  // resident decode workgroups per CU
+int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                                  int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
                                  hipStream_t stream);
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t stream);
 
 }  // namespace attn

@@ -11,17 +11,20 @@
 //    over resident CTAs; partial (m, l, O) states merged by rescaling to the
 //    common max.  The work split itself lives in plan.h.
 //
-// gfx950 mapping.  A workgroup is 8 wave64s.  Inside a piece (one (b, kv head)
-// context range) the waves take 32-key blocks round-robin and never
-// synchronise until the piece ends.  Per block a wave
-//   1. loads K and V rows straight from HBM into registers in the MFMA operand
-//      layout (16-byte loads; lane = key row, lane group = 8-wide d chunk);
-//   2. BMM1 on v_mfma_f32_16x16x32_bf16 with A = K (16 keys x 32 d), B = Q^T
-//      (32 d x 16 heads, rows >= G are zero): S^T lands with the head index on
-//      lanes and four consecutive keys per lane;
+// gfx950 mapping.  A workgroup is 8 wave64s (4 at Hsz = 256).  Inside a piece
+// (one (b, kv head) context range) the waves take 32-key blocks round-robin
+// and never synchronise with each other until the piece ends.  Per block a wave
+//   1. streams the K and V rows from HBM with fully coalesced, non-temporal
+//      16-byte loads (each load instruction covers whole 128-byte lines; a
+//      measured 6.7-7.1 TB/s pattern, against ~6.0 TB/s when each instruction
+//      takes 64 bytes of 16 rows) into registers, while the previous block is
+//      being computed, and parks them in its own LDS stage;
+//   2. BMM1 on v_mfma_f32_16x16x32_bf16 with A = K (16 keys x 32 d, read from
+//      the stage), B = Q^T (32 d x 16 heads, rows >= G are zero): S^T lands
+//      with the head index on lanes and four consecutive keys per lane;
 //   3. online softmax in the log2 domain; the row max over the block needs two
 //      cross-lane steps (lanes 16 and 32 apart);
-//   4. V^T without LDS: an MFMA against a 0/1 selection matrix re-distributes a
+//   4. V^T by MFMA: a product with a 0/1 selection matrix re-distributes a
 //      16-key x 32-d tile of V so that each lane holds four consecutive keys of
 //      one d (exact: one product by 1.0 plus zeros);
 //   5. BMM2 on MFMA with A = V^T (16 d x 32 keys), B = P^T (32 keys x 16 heads);
@@ -29,10 +32,10 @@
 //      ~2^-17 relative accuracy instead of bf16's 2^-9.
 //  The key order inside each MFMA contraction is chosen so that the lanes that
 //  hold S^T after step 2 already hold the P^T operand of step 5 and the lanes
-//  of step 4's output already hold the V^T operand: no shuffles and no LDS in
-//  the streaming loop.  At the end of a piece the 8 wave states are merged
-//  through LDS (max, rescale, tree sum) and written either as the final output
-//  or as a partial slot for the merge kernel.
+//  of step 4's output already hold the V^T operand: no shuffles beyond the two
+//  row-max steps.  At the end of a piece the wave states are merged through
+//  LDS (max, rescale, tree sum) and written either as the final output or as a
+//  partial slot for the merge kernel.
 #include "common.h"
 
 namespace attn {
@@ -56,15 +59,143 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// Waves per workgroup: 8 while a wave's 32-key K/V staging fits (LDS), 4 at Hsz = 256.
 template <int HSZ>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_tiles_kernel(const DecodeParams p) {
-    constexpr int NS = HSZ / 32;  // MFMA K steps over d
-    constexpr int ND = HSZ / 16;  // 16-wide d blocks of the output
-    constexpr int W = kDecodeWaves;
+struct DecodeCfg {
+    static constexpr int W = HSZ == 256 ? 4 : 8;
+    static constexpr int NS = HSZ / 32;                  // MFMA K steps over d
+    static constexpr int ND = HSZ / 16;                  // 16-wide d blocks of the output
+    static constexpr int CH = HSZ / 8;                   // 16-byte chunks per row
+    static constexpr int RS = HSZ + 8;                   // staged row stride (bf16), 16 B pad
+    static constexpr int LOADS = 2 * kKeysPerBlock * CH / 64;  // 16-byte loads per lane per block (K + V)
+    static constexpr int STAGE = 2 * kKeysPerBlock * RS;       // bf16 per wave: K rows then V rows
+};
+
+// One wave's next block in registers: fully coalesced 16-byte loads (lane l of
+// load j reads chunk (64j + l) of the block, row-major over keys), marked
+// non-temporal because every byte is used exactly once.  Rows past klast are
+// clamped re-reads of row klast (their scores are masked later).
+template <int HSZ>
+struct Staged {
+    u32x4 r[DecodeCfg<HSZ>::LOADS];
+};
+
+template <int HSZ>
+__device__ __forceinline__ void load_block(Staged<HSZ> &st, const uint16_t *kbase, const uint16_t *vbase, int key0,
+                                           int klast, int lane) {
+    using C = DecodeCfg<HSZ>;
+    constexpr int HALF = C::LOADS / 2;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+        const int c = 64 * j + lane;
+        int key = key0 + c / C::CH;
+        key = key < klast ? key : klast;
+        const int64_t off = (int64_t)key * HSZ + 8 * (c % C::CH);
+        st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off));
+        st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vbase + off));
+    }
+}
+
+// Registers -> this wave's LDS stage, rows padded by 16 bytes (row-parallel
+// 16-byte reads of the MFMA operands then hit distinct banks).
+template <int HSZ>
+__device__ __forceinline__ void store_block(const Staged<HSZ> &st, uint16_t *stage, int lane) {
+    using C = DecodeCfg<HSZ>;
+    constexpr int HALF = C::LOADS / 2;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+        const int c = 64 * j + lane;
+        const int row = c / C::CH, ch = c % C::CH;
+        *reinterpret_cast<u32x4 *>(stage + row * C::RS + 8 * ch) = st.r[j];
+        *reinterpret_cast<u32x4 *>(stage + (kKeysPerBlock + row) * C::RS + 8 * ch) = st.r[HALF + j];
+    }
+}
+
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// BMM1 -> online softmax -> BMM2 for one staged 32-key block of one wave.
+template <int HSZ>
+__device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[HSZ / 32],
+                                              const bf16x8 (&sel)[2], int key0, int klast, int col, int grp,
+                                              float scale_log2, float &m_run, float &l_run,
+                                              f32x4 (&oacc)[HSZ / 16]) {
+    using C = DecodeCfg<HSZ>;
+    constexpr int NS = C::NS;
+    constexpr int ND = C::ND;
+    const float NEG_INF = -__builtin_inff();
+    const uint16_t *krow = stage + col * C::RS + 8 * grp;                        // key col of 16-key block 0
+    const uint16_t *vrow = stage + (kKeysPerBlock + col) * C::RS + 8 * grp;
+    // BMM1: S^T[key][g] for keys key0 + 16kb + 4grp + i in lane (g = col, grp)
+    f32x4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sc[kb] = mfma_bf16(lds_row8(krow + 16 * kb * C::RS + 32 * s), qop[s], sc[kb]);
+    }
+    float x[8];
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * kb + 4 * grp + i;
+            const float xv = key <= klast ? sc[kb][i] * scale_log2 : NEG_INF;
+            x[4 * kb + i] = xv;
+            mx = fmaxf(mx, xv);
+        }
+    mx = wave_max_over_groups(mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: every processed block holds a valid key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps = 0.f;
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(x[i] - m_new);
+        ps += pv;
+        const __bf16 hi = (__bf16)pv;
+        phi[i] = hi;
+        plo[i] = (__bf16)(pv - (float)hi);
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+    // V^T via selection MFMAs, then BMM2 with the hi and lo parts of P
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const bf16x8 v0 = lds_row8(vrow + 32 * s);
+        const bf16x8 v1 = lds_row8(vrow + 16 * C::RS + 32 * s);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 t0 = mfma_bf16(v0, sel[h], z);
+            const f32x4 t1 = mfma_bf16(v1, sel[h], z);
+            bf16x8 vt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vt[i] = (__bf16)t0[i];
+                vt[4 + i] = (__bf16)t1[i];
+            }
+            const int db = 2 * s + h;
+            oacc[db] = mfma_bf16(vt, phi, oacc[db]);
+            oacc[db] = mfma_bf16(vt, plo, oacc[db]);
+        }
+    }
+}
+
+template <int HSZ>
+__global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
+    using C = DecodeCfg<HSZ>;
+    constexpr int NS = C::NS;
+    constexpr int ND = C::ND;
+    constexpr int W = C::W;
     constexpr int OSTRIDE = HSZ + 4;  // padded LDS row of the cross-wave reduction
-    extern __shared__ float smem[];
-    float *sm_m = smem;           // [W][16]
-    float *sm_l = smem + W * 16;  // [W][16]
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    // streaming phase: one K/V stage per wave; piece epilogue: the reduction buffers
+    uint16_t *stages = reinterpret_cast<uint16_t *>(smem);
+    float *sm_m = smem;               // [W][16]
+    float *sm_l = smem + W * 16;      // [W][16]
     float *sm_o = smem + 2 * W * 16;  // [W/2][G][OSTRIDE]
 
     const int lane = threadIdx.x & 63;
@@ -75,6 +206,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_tiles_kernel(const D
     const LeanPlan &pl = p.plan;
     const int G = p.G;
     const float NEG_INF = -__builtin_inff();
+    uint16_t *stage = stages + wave * C::STAGE;
 
     // 0/1 selection operands: sel[h] picks d = 16h + col out of a 32-d chunk.
     bf16x8 sel[2];
@@ -108,74 +240,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_tiles_kernel(const D
 
         const int nblk = (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
         const int klast = pc.key_end - 1;
-        for (int blk = wave; blk < nblk; blk += W) {
-            const int key0 = pc.key_begin + blk * kKeysPerBlock;
-            bf16x8 kr[2][NS], vr[2][NS];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                int key = key0 + 16 * kb + col;
-                key = key < klast ? key : klast;  // rows past the piece are re-reads, masked below
-                const int64_t off = (int64_t)key * HSZ + 8 * grp;
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    kr[kb][s] = load_row8(kbase + off + 32 * s);
-                    vr[kb][s] = load_row8(vbase + off + 32 * s);
-                }
-            }
-            // BMM1: S^T[key][g] for keys key0 + 16kb + 4grp + i in lane (g = col, grp)
-            f32x4 sc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) sc[kb] = mfma_bf16(kr[kb][s], qop[s], sc[kb]);
-            }
-            float x[8];
-            float mx = NEG_INF;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = key0 + 16 * kb + 4 * grp + i;
-                    const float xv = key <= klast ? sc[kb][i] * p.scale_log2 : NEG_INF;
-                    x[4 * kb + i] = xv;
-                    mx = fmaxf(mx, xv);
-                }
-            mx = wave_max_over_groups(mx);
-            const float m_new = fmaxf(m_run, mx);  // finite: every block holds a valid key
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float ps = 0.f;
-            bf16x8 phi, plo;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(x[i] - m_new);
-                ps += pv;
-                const __bf16 hi = (__bf16)pv;
-                phi[i] = hi;
-                plo[i] = (__bf16)(pv - (float)hi);
-            }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-            // V^T via selection MFMAs, then BMM2 with the hi and lo parts of P
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    const f32x4 t0 = mfma_bf16(vr[0][s], sel[h], z);
-                    const f32x4 t1 = mfma_bf16(vr[1][s], sel[h], z);
-                    bf16x8 vt;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        vt[i] = (__bf16)t0[i];
-                        vt[4 + i] = (__bf16)t1[i];
-                    }
-                    const int db = 2 * s + h;
-                    oacc[db] = mfma_bf16(vt, phi, oacc[db]);
-                    oacc[db] = mfma_bf16(vt, plo, oacc[db]);
-                }
+        // Each wave owns blocks wave, wave + W, ...; block n + W is loading
+        // while block n is computed out of the wave's LDS stage.  LDS traffic
+        // of one wave executes in issue order, so no barrier is needed.
+        Staged<HSZ> st;
+        int blk = wave;
+        if (blk < nblk) load_block<HSZ>(st, kbase, vbase, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        for (; blk < nblk; blk += W) {
+            store_block<HSZ>(st, stage, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (blk + W < nblk)
+                load_block<HSZ>(st, kbase, vbase, pc.key_begin + (blk + W) * kKeysPerBlock, klast, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, klast, col, grp, p.scale_log2,
+                               m_run, l_run, oacc);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
 
         // ---- merge the W wave states of this piece ----
@@ -235,28 +316,43 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_tiles_kernel(const D
     }
 }
 
-// One workgroup per (segment, head of the group, 32-wide d chunk).  Segments
-// finished inside one CTA are skipped; empty segments (L_b = 0) get zero rows.
+// Merge of split heads.  One workgroup per (segment, head of the group,
+// 16-wide d chunk); its 256 threads are 16 partial lanes x 16 d.  Each thread
+// folds the partials i = lane, lane+16, ... into a running (max, sum, O) with
+// the same rescale the tile kernel uses, four partials per round so their
+// loads are in flight together; the 16 lane states are then folded through
+// LDS.  Segments finished inside one CTA are skipped; empty segments
+// (L_b = 0) get zero rows.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeLanesPerPartial = 32;
-constexpr int kMergeGroups = kMergeThreads / kMergeLanesPerPartial;
+constexpr int kMergeD = 16;
+constexpr int kMergeLanes = kMergeThreads / kMergeD;
+constexpr int kMergeUnroll = 4;
+
+__device__ __forceinline__ void fold_state(float &M, float &L, float &O, float m2, float l2, float o2) {
+    const float Mn = fmaxf(M, m2);
+    if (Mn == -__builtin_inff()) return;  // both empty
+    const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(m2 - Mn);
+    L = L * a + l2 * b;
+    O = O * a + o2 * b;
+    M = Mn;
+}
 
 template <int HSZ>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeParams p) {
-    __shared__ float red_m[kMergeGroups];
-    __shared__ float red_o[kMergeGroups][kMergeLanesPerPartial];
-    __shared__ float red_l[kMergeGroups];
+    __shared__ float red_m[kMergeLanes][kMergeD];
+    __shared__ float red_l[kMergeLanes][kMergeD];
+    __shared__ float red_o[kMergeLanes][kMergeD];
     const LeanPlan &pl = p.plan;
     const int s = blockIdx.x, g = blockIdx.y, dc = blockIdx.z;
     const int b = s / pl.KH, kh = s % pl.KH;
     const int G = p.G;
     const int tid = threadIdx.x;
-    const int pgrp = tid / kMergeLanesPerPartial, dd = tid % kMergeLanesPerPartial;
-    const int d = dc * kMergeLanesPerPartial + dd;
+    const int lane = tid / kMergeD, dd = tid % kMergeD;
+    const int d = dc * kMergeD + dd;
     float *orow = p.out + ((int64_t)b * p.Hq + kh * G + g) * HSZ;
     const int nb = plan_tiles_per_segment(pl, b);
     if (nb == 0) {
-        if (pgrp == 0) orow[d] = 0.f;
+        if (lane == 0) orow[d] = 0.f;
         return;
     }
     const int64_t seg_begin = pl.tile_prefix[b] + (int64_t)kh * nb;
@@ -267,42 +363,43 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
     const int slot0 = plan_slot(pl, c_lo, seg_begin);
     const float NEG_INF = -__builtin_inff();
 
-    float mx = NEG_INF;
-    for (int i = pgrp; i < k; i += kMergeGroups) {
-        const int slot = i == 0 ? slot0 : 2 * (c_lo + i);
-        mx = fmaxf(mx, p.ws[(int64_t)slot * p.slot_floats + G * HSZ + g]);
-    }
-    if (dd == 0) red_m[pgrp] = mx;
-    __syncthreads();
-    float M = NEG_INF;
+    float M = NEG_INF, L = 0.f, O = 0.f;
+    for (int i0 = lane; i0 < k; i0 += kMergeLanes * kMergeUnroll) {
+        float mv[kMergeUnroll], lv[kMergeUnroll], ov[kMergeUnroll];
 #pragma unroll
-    for (int j = 0; j < kMergeGroups; ++j) M = fmaxf(M, red_m[j]);
-
-    float acc = 0.f, lsum = 0.f;
-    for (int i = pgrp; i < k; i += kMergeGroups) {
-        const int slot = i == 0 ? slot0 : 2 * (c_lo + i);
-        const float *sp = p.ws + (int64_t)slot * p.slot_floats;
-        const float f = __builtin_amdgcn_exp2f(sp[G * HSZ + g] - M);
-        acc += f * sp[g * HSZ + d];
-        lsum += f * sp[G * HSZ + G + g];
-    }
-    red_o[pgrp][dd] = acc;
-    if (dd == 0) red_l[pgrp] = lsum;
-    __syncthreads();
-    if (pgrp == 0) {
-        float o = 0.f, l = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMergeGroups; ++j) {
-            o += red_o[j][dd];
-            l += red_l[j];
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int i = i0 + u * kMergeLanes;
+            mv[u] = NEG_INF;
+            lv[u] = 0.f;
+            ov[u] = 0.f;
+            if (i < k) {
+                const int slot = i == 0 ? slot0 : 2 * (c_lo + i);
+                const float *sp = p.ws + (int64_t)slot * p.slot_floats;
+                mv[u] = sp[G * HSZ + g];
+                lv[u] = sp[G * HSZ + G + g];
+                ov[u] = sp[g * HSZ + d];
+            }
         }
-        orow[d] = o / l;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) fold_state(M, L, O, mv[u], lv[u], ov[u]);
+    }
+    red_m[lane][dd] = M;
+    red_l[lane][dd] = L;
+    red_o[lane][dd] = O;
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 1; j < kMergeLanes; ++j) fold_state(M, L, O, red_m[j][dd], red_l[j][dd], red_o[j][dd]);
+        orow[d] = O / L;
     }
 }
 
 template <int HSZ>
 size_t decode_tiles_lds_bytes(int G) {
-    return (size_t)(2 * kDecodeWaves * 16 + (kDecodeWaves / 2) * G * (HSZ + 4)) * sizeof(float);
+    using C = DecodeCfg<HSZ>;
+    const size_t stage = (size_t)C::W * C::STAGE * sizeof(uint16_t);
+    const size_t reduce = (size_t)(2 * C::W * 16 + (C::W / 2) * G * (HSZ + 4)) * sizeof(float);
+    return stage > reduce ? stage : reduce;
 }
 
 size_t tiles_lds_bytes(int Hsz, int G) {
@@ -321,13 +418,13 @@ hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(decode_tiles_kernel<HSZ>, dim3(p.plan.P), dim3(kDecodeWaves * 64), lds, stream, p);
+    hipLaunchKernelGGL(decode_tiles_kernel<HSZ>, dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds, stream, p);
     return hipGetLastError();
 }
 
 template <int HSZ>
 hipError_t launch_merge_t(const DecodeParams &p, hipStream_t stream) {
-    dim3 grid(p.plan.B * p.plan.KH, p.G, HSZ / kMergeLanesPerPartial);
+    dim3 grid(p.plan.B * p.plan.KH, p.G, HSZ / kMergeD);
     hipLaunchKernelGGL(decode_merge_kernel<HSZ>, grid, dim3(kMergeThreads), 0, stream, p);
     return hipGetLastError();
 }
@@ -339,13 +436,21 @@ int occupancy_t(int G) {
     if (lds > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ>, kDecodeWaves * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ>, DecodeCfg<HSZ>::W * 64,
                                                      decode_tiles_lds_bytes<HSZ>(G)) != hipSuccess)
         return 1;
     return blocks > 0 ? blocks : 1;
 }
 
 }  // namespace
+
+int decode_tile_keys(int Hsz) {
+    switch (Hsz) {
+        case 64: return DecodeCfg<64>::W * kKeysPerBlock;
+        case 128: return DecodeCfg<128>::W * kKeysPerBlock;
+        default: return DecodeCfg<256>::W * kKeysPerBlock;
+    }
+}
 
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream) {
     switch (Hsz) {

@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA decode/prefill library on one MI355X.
+
+A step is one ``attn_decode`` call (plan, LeanTile kernel, merge kernel) on the
+Llama-3-8B-shaped decode workload: B=16, Hq=32, KH=8 (G=4), Hsz=128, every request
+at 8192 cached tokens, bf16 K/V ~ N(0,1), fp32 output.  ``value`` is the achieved HBM
+bandwidth in algorithmic bytes (every cached K and V byte, the query and the output,
+each counted once) per second of step time, measured with the inputs already resident
+in HBM.  The K/V caches are rotated over enough copies that each step reads bytes the
+256 MiB last-level cache does not hold from the previous step.
+
+The same run also times: the tile kernel alone (HIP events recorded on the launch
+stream around it -> the ``roofline`` object), the long-context MQA decode (x1 and x8
+scores), the ragged batch, causal prefill (bf16/fp16 MFMA TFLOP/s), a plain copy of
+known size (the practical streaming ceiling), and the fp64 CPU oracle on the headline
+workload (``cpu_baseline``).  One JSON line goes to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30  # rotate K/V copies until each step's working set exceeds MALL + L2
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev: int) -> None:
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for f in ["decode.hip", "plan.h", "common.h"]:
+        with open(os.path.join(ROOT, "attention_gqa_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(name: str, launches_bytes: float):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_sources_digest:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_sources_digest():
+        return None
+    return float(m_bytes.group(1))
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True):
+    import torch
+
+    import attention_gqa_decode_amd as A
+    from attention_gqa_decode_amd import accounting as acc
+    from attention_gqa_decode_amd import workloads as W
+
+    q, k, v, sl = W.decode_inputs(shape, device="cuda")
+    sl = sl.tolist()
+    kv_read = 2 * shape.KH * sum(sl) * shape.Hsz * 2
+    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(kv_read, 1)))) if rotate else 1
+    ks = [k] + [k.clone() for _ in range(copies - 1)]
+    vs = [v] + [v.clone() for _ in range(copies - 1)]
+    out = torch.empty((shape.B, shape.Hq, shape.Hsz), dtype=torch.float32, device="cuda")
+    scale = shape.score_mult / math.sqrt(shape.Hsz) if shape.score_mult != 1.0 else 0.0
+    for i in range(warmup):
+        A.attn_decode_ex(q, ks[i % copies], vs[i % copies], sl, out=out, scale=scale)
+    torch.cuda.synchronize()
+    evs = [(hev.create(), hev.create()) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        A.attn_decode_ex(q, ks[i % copies], vs[i % copies], sl, out=out, scale=scale,
+                         ev_tiles_begin=evs[i][0], ev_tiles_end=evs[i][1])
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    kern = [hev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    nbytes = acc.decode_bytes(sl, shape.B, shape.Hq, shape.KH, shape.Hsz)
+    kern_ms = sum(kern) / len(kern)
+    res = {
+        "workload": shape.name, "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
+        "sum_kvsl": int(sum(sl)), "max_kvsl": int(max(sl)), "score_mult": shape.score_mult,
+        "kv_copies_rotated": copies, "bytes_per_step": nbytes,
+        "us_per_step": step_ms * 1e3, "GBps": nbytes / (step_ms * 1e-3) / 1e9,
+        "tile_kernel_us": kern_ms * 1e3, "tile_kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9,
+    }
+    res["frac_of_peak"] = res["GBps"] / PEAK_HBM_GBPS
+    del q, ks, vs, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+
+    import attention_gqa_decode_amd as A
+    from attention_gqa_decode_amd import accounting as acc
+    from attention_gqa_decode_amd import workloads as W
+
+    s = W.prefill_workload()
+    q, k, v = W.prefill_inputs(s, device="cuda")
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        A.attn_prefill_causal(q, k, v, out=out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        A.attn_prefill_causal(q, k, v, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    fl = acc.prefill_causal_flops(s.B, s.ISL, s.Hq, s.Hsz)
+    tf = fl / (ms * 1e-3) / 1e12
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"workload": "prefill_causal", "B": s.B, "ISL": s.ISL, "Hq": s.Hq, "KH": s.KH, "Hsz": s.Hsz,
+            "flops_per_step": fl, "us_per_step": ms * 1e3, "TFLOPs": tf, "mfma_frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+
+
+def bench_copy_probe(steps: int):
+    import torch
+
+    import attention_gqa_decode_amd as A
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    A.attn_hbm_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        A.attn_hbm_copy_probe(src, dst)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    big = torch.empty(4 * n, dtype=torch.uint8, device="cuda")  # 4 GiB: far past the last-level cache
+    big.fill_(3)
+    A.attn_hbm_read_probe(big, sink)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        A.attn_hbm_read_probe(big, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    rms = t0.elapsed_time(t1) / steps
+    del src, dst, big, sink
+    torch.cuda.empty_cache()
+    return {"copy_bytes": n, "copy_us": ms * 1e3, "copy_read_plus_write_GBps": 2 * n / (ms * 1e-3) / 1e9,
+            "read_bytes": 4 * n, "read_us": rms * 1e3, "read_GBps": 4 * n / (rms * 1e-3) / 1e9}
+
+
+def cpu_baseline(shape, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on the headline workload (whole steps, repeated)."""
+    import oracle
+    from attention_gqa_decode_amd import accounting as acc
+    from attention_gqa_decode_amd import workloads as W
+    from attention_gqa_decode_amd.workloads import bits
+
+    q, k, v, sl = W.decode_inputs(shape, device="cuda")
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    del q, k, v
+    sl = sl.numpy()
+    scale = 1 / math.sqrt(shape.Hsz)
+    reps, t_start = 0, time.perf_counter()
+    while True:
+        oracle.decode(qb, kb, vb, sl, shape.Hq, shape.KH, scale)
+        reps += 1
+        el = time.perf_counter() - t_start
+        if el >= budget_s / 3 or reps >= 20:
+            break
+    per = el / reps
+    nbytes = acc.decode_bytes(sl.tolist(), shape.B, shape.Hq, shape.KH, shape.Hsz)
+    return {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full {shape.name} decode step(s) (all {shape.B * shape.Hq} heads), "
+                      f"{per:.3f} s per step, fp64 plain C + OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--headline-only", action="store_true", help="time only the headline decode workload")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs attention on a single MI355X; "
+              "multi-GPU sharding (heads / requests / KV sequence) is a design note only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_gqa_decode_amd as A
+    from attention_gqa_decode_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    hev = HipEvents()
+    cus, lds = A.attn_device_info()
+    log(f"device: {torch.cuda.get_device_name(0)}, {cus} CUs, {lds} B LDS/CU")
+
+    head = W.decode_workload("llama3_8b")
+    log("decode llama3_8b ...")
+    r = bench_decode(head, args.steps, args.warmup, hev)
+    log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, tile kernel {r['tile_kernel_us']:.1f} us")
+    others = []
+    probe = None
+    prefill = None
+    if not args.headline_only:
+        for name in ["long_mqa", "long_mqa_x8", "ragged"]:
+            log(f"decode {name} ...")
+            o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
+            log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
+            others.append(o)
+        log("prefill ...")
+        prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
+        log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
+        probe = bench_copy_probe(max(3, args.steps // 5))
+        log(f"copy probe {probe['copy_read_plus_write_GBps']:.0f} GB/s, read probe {probe['read_GBps']:.0f} GB/s")
+    cpu = None
+    if not args.skip_cpu:
+        log("cpu oracle baseline ...")
+        cpu = cpu_baseline(head)
+        log(f"  {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
+
+    traffic = committed_traffic("decode_tiles_llama3_8b", r["bytes_per_step"])
+    line = {
+        "metric": "decode attn achieved HBM GB/s (% peak) + us/step; prefill MFMA TFLOP/s",
+        "value": round(r["GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["us_per_step"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_gqa_decode", "B": head.B, "Hq": head.Hq, "KH": head.KH, "Hsz": head.Hsz,
+                   "kvsl": head.seqlens[0], "out_dtype": "fp32", "parallelism": "single_gpu"},
+        "frac_of_peak_hbm": round(r["frac_of_peak"], 4),
+        "us_per_step": round(r["us_per_step"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(r["tile_kernel_GBps"], 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(r["tile_kernel_GBps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_tiles_kernel<128>",
+                     "kernel_us": round(r["tile_kernel_us"], 2)},
+        "cpu_baseline": cpu,
+        "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
+                                   for o in others],
+        "prefill": prefill,
+        "hbm_probes": probe,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

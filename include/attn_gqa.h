@@ -153,6 +153,14 @@ int attn_decode_plan(const int32_t *seqlens, int B, int KH, int tile_keys, int n
  */
 int attn_hbm_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/*
+ * attn_hbm_read_probe -- reads `bytes` (a multiple of 16) from src once with
+ * 16-byte vector loads and folds them into a value that is written to the
+ * 4-byte device word `sink` only when it equals a fixed sentinel.  Its time
+ * is the practical streaming read rate, the ceiling the decode kernel chases.
+ */
+int attn_hbm_read_probe(const void *src, size_t bytes, void *sink, hipStream_t stream);
+
 /* Compute units and LDS bytes per compute unit of the current device. */
 int attn_device_info(int *num_cus, int *lds_bytes_per_cu);
 

@@ -43,6 +43,8 @@ def _load():
     if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_bf16_decode.argtypes = [_P, _P, _I64]
@@ -72,6 +74,11 @@ def _u16(a) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def bf16_to_f64(bits) -> np.ndarray:

@@ -44,6 +44,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops below will use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* bf16 is the upper half of an IEEE-754 binary32; widening is exact. */
 double oracle_bf16_to_f64(uint16_t bits) {
