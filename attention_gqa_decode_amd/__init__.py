@@ -22,6 +22,8 @@ ATTN_ERR_WORKSPACE = -5
 ATTN_ERR_HIP = -6
 ATTN_MAX_BATCH = 256
 ATTN_MAX_GROUP = 16
+ATTN_MAX_CTAS = 4096
+ATTN_DECODE_COUNTER_BYTES = 98304
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -138,8 +140,10 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
                    workspace=None, ev_tiles_begin=None, ev_tiles_end=None, stream=None):
     """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
 
-    ``workspace`` is an optional CUDA tensor used as the partial-state buffer;
-    ``ev_tiles_begin/end`` are optional raw ``hipEvent_t`` handles (ints).
+    ``workspace`` is an optional CUDA tensor used as the partial-state buffer; its first
+    ``ATTN_DECODE_COUNTER_BYTES`` bytes must be zero before its first use (allocate it with
+    ``torch.zeros``), and each call leaves them zero.  ``ev_tiles_begin/end`` are optional
+    raw ``hipEvent_t`` handles (ints) recorded around the decode kernel.
     """
     import torch
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
@@ -167,6 +171,48 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     a.ev_tiles_end = ev_tiles_end
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
     return out
+
+
+class PreparedDecode:
+    """``attn_decode_ex`` with its argument block marshalled once, for tight launch loops.
+
+    The tensors are validated and their addresses packed when the object is built;
+    calling it only passes the packed block and a stream handle to ``attn_decode_ex``.
+    The caller keeps the tensors alive and unchanged in shape while the object is used.
+    """
+
+    def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0):
+        for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+            _bf16_cuda(n, t)
+        B, Hq, Hsz = q.shape
+        KH, S = k_cache.shape[1], k_cache.shape[2]
+        self._sl = _host_seqlens(seqlens)
+        if len(self._sl) != B:
+            raise ValueError("seqlens must have B entries")
+        if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
+            raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
+        if tuple(out.shape) != (B, Hq, Hsz) or not out.is_cuda or not out.is_contiguous():
+            raise ValueError("out must be a contiguous fp32 CUDA tensor [B][Hq][Hsz]")
+        a = attn_decode_args()
+        a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+        a.seqlens, a.out = self._sl.ctypes.data, out.data_ptr()
+        a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
+        a.kv_stride = S
+        a.scale = float(scale)
+        a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+        self._args = a
+        self._ref = ctypes.byref(a)
+        self._fn = lib().attn_decode_ex
+
+    def set_events(self, begin=None, end=None):
+        """Raw ``hipEvent_t`` handles to record around the decode kernel (None = none)."""
+        self._args.ev_tiles_begin = begin
+        self._args.ev_tiles_end = end
+
+    def __call__(self, stream_handle: int) -> None:
+        st = self._fn(self._ref, stream_handle)
+        if st != ATTN_OK:
+            _check(st)
 
 
 def attn_decode_workspace_bytes(B: int, Hq: int, KH: int, Hsz: int, num_ctas: int = 0) -> int:

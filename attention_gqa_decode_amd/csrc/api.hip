@@ -15,6 +15,8 @@
 #include "common.h"
 
 static_assert(ATTN_MAX_GROUP == attn::kMaxGroup, "group limit mismatch");
+static_assert(ATTN_MAX_CTAS == attn::kMaxCtas, "CTA limit mismatch");
+static_assert(ATTN_DECODE_COUNTER_BYTES == attn::kCounterBytes, "counter region mismatch");
 
 namespace {
 
@@ -86,6 +88,9 @@ int library_workspace(hipStream_t stream, size_t bytes, void **ptr) {
             return fail_hip(e, "hipMalloc(workspace)");
         }
         w.bytes = grow;
+        // the arrival counters must start at zero; the kernel leaves them zero
+        e = attn::launch_zero_fill(w.ptr, grow, stream);
+        if (e != hipSuccess) return fail_hip(e, "workspace zero fill");
     }
     *ptr = w.ptr;
     return ATTN_OK;
@@ -134,12 +139,6 @@ bool any_split_segment(const LeanPlan &p) {
     return false;
 }
 
-bool any_empty_segment(const LeanPlan &p) {
-    for (int b = 0; b < p.B; ++b)
-        if (p.seqlen[b] == 0) return true;
-    return false;
-}
-
 }  // namespace
 
 extern "C" {
@@ -164,7 +163,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas)
     const int G = Hq / KH;
     int P = num_ctas;
     if (P == 0 && device_default_ctas(Hsz, G, &P) != ATTN_OK) return 0;
-    return (size_t)2 * P * attn::decode_slot_floats(G, Hsz) * sizeof(float);
+    if (P > attn::kMaxCtas) return 0;
+    return attn::decode_workspace_bytes(P, G, Hsz);
 }
 
 int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
@@ -178,6 +178,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         return fail(ATTN_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
     if (a->kv_stride < 0) return fail(ATTN_ERR_SHAPE, "kv_stride=%lld is negative", (long long)a->kv_stride);
     if (a->tile_keys < 0 || a->num_ctas < 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be >= 0");
+    if (a->num_ctas > attn::kMaxCtas) return fail(ATTN_ERR_UNSUPPORTED, "num_ctas=%d exceeds %d", a->num_ctas, attn::kMaxCtas);
     if (!(a->scale == a->scale) || isinf(a->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
     if (a->workspace && !aligned16(a->workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
 
@@ -204,46 +205,44 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.scale_log2 = scale * 1.4426950408889634f;
 
     int P = a->num_ctas;
-    if (P > 0 && a->workspace && (size_t)2 * P * p.slot_floats * sizeof(float) > a->workspace_bytes)
+    if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, G, a->Hsz) > a->workspace_bytes)
         return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for num_ctas=%d", a->workspace_bytes,
-                    (size_t)2 * P * p.slot_floats * sizeof(float), P);
+                    attn::decode_workspace_bytes(P, G, a->Hsz), P);
 
     // ---- argument checks done; HIP calls from here on ----
     if (P == 0) {
         st = device_default_ctas(a->Hsz, G, &P);
         if (st != ATTN_OK) return st;
+        if (P > attn::kMaxCtas) P = attn::kMaxCtas;
     }
-    if (p.plan.N > 0 && P > p.plan.N) P = (int)p.plan.N;
+    if (P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;  // no empty CTA; one CTA zeroes an all-empty batch
     p.plan.P = P;
+    p.counters = nullptr;
 
-    const bool split = p.plan.N > 0 && any_split_segment(p.plan);
-    if (split) {
-        const size_t need = (size_t)2 * P * p.slot_floats * sizeof(float);
+    if (p.plan.N > 0 && any_split_segment(p.plan)) {
+        const size_t need = attn::decode_workspace_bytes(P, G, a->Hsz);
+        char *w = nullptr;
         if (a->workspace) {
             if (a->workspace_bytes < need)
                 return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed", a->workspace_bytes, need);
-            p.ws = static_cast<float *>(a->workspace);
+            w = static_cast<char *>(a->workspace);
         } else {
-            void *w = nullptr;
-            st = library_workspace(stream, need, &w);
+            void *lw = nullptr;
+            st = library_workspace(stream, need, &lw);
             if (st != ATTN_OK) return st;
-            p.ws = static_cast<float *>(w);
+            w = static_cast<char *>(lw);
         }
+        p.counters = reinterpret_cast<int *>(w);
+        p.ws = reinterpret_cast<float *>(w + attn::kCounterBytes);
     }
 
     hipError_t e;
-    if (p.plan.N > 0) {
-        if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
-            return fail_hip(e, "hipEventRecord(begin)");
-        e = attn::launch_decode_tiles(p, a->Hsz, stream);
-        if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
-        if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
-            return fail_hip(e, "hipEventRecord(end)");
-    }
-    if (split || any_empty_segment(p.plan)) {
-        e = attn::launch_decode_merge(p, a->Hsz, stream);
-        if (e != hipSuccess) return fail_hip(e, "decode merge kernel launch");
-    }
+    if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
+        return fail_hip(e, "hipEventRecord(begin)");
+    e = attn::launch_decode_tiles(p, a->Hsz, stream);
+    if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
+    if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
+        return fail_hip(e, "hipEventRecord(end)");
     return ATTN_OK;
 }
 

@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxGroup = 16;       // query heads per kv head held by one workgroup (MFMA N = 16)
 constexpr int kKeysPerBlock = 32;   // keys one wave consumes per step (two 16-key MFMA row blocks)
@@ -23,6 +24,7 @@ struct DecodeParams {
     const uint16_t *v;   // bf16 [B][KH][S][Hsz]
     float *out;          // fp32 [B][Hq][Hsz]
     float *ws;           // partial slots, each slot_floats long
+    int *counters;       // arrival counters [kMergeLevels][2 * kMaxCtas], zero between calls
     int64_t kv_stride;   // S
     int Hq;
     int G;
@@ -34,9 +36,23 @@ struct DecodeParams {
 // Partial slot layout: O[G][Hsz] unnormalised, then m[G] (log2 domain), then l[G].
 inline int decode_slot_floats(int G, int Hsz) { return (G * Hsz + 2 * G + 3) & ~3; }
 
+// Split heads are merged inside the tile kernel by a tree of fan-in kMergeFanIn:
+// the last CTA to arrive at a group merges it.  kMergeLevels levels cover
+// kMergeFanIn^kMergeLevels = kMaxCtas partials of one head.
+constexpr int kMergeFanIn = 16;
+constexpr int kMergeLevels = 3;
+constexpr int kMaxCtas = 4096;
+
+// Workspace layout: int counters[kMergeLevels][2 * kMaxCtas] (a fixed-size
+// region, so its place never depends on P), then float slots[2P][slot_floats].
+constexpr size_t kCounterBytes = (size_t)kMergeLevels * 2 * kMaxCtas * sizeof(int);
+inline size_t decode_workspace_bytes(int P, int G, int Hsz) {
+    return kCounterBytes + (size_t)2 * P * decode_slot_floats(G, Hsz) * sizeof(float);
+}
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeParams &p, int Hsz, hipStream_t stream);
+hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int G);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,

@@ -1,4 +1,4 @@
-// decode.hip -- GQA decode on gfx950: LeanTile tile kernel and partial-state merge kernel.
+// decode.hip -- GQA decode on gfx950: the LeanTile kernel, with the merge of split heads fused in.
 //
 // What runs (sources by page title and section):
 //  * co-design page "장문 컨텍스트 추론을 위한 어텐션 공동 설계", sections
@@ -34,8 +34,13 @@
 //  hold S^T after step 2 already hold the P^T operand of step 5 and the lanes
 //  of step 4's output already hold the V^T operand: no shuffles beyond the two
 //  row-max steps.  At the end of a piece the wave states are merged through
-//  LDS (max, rescale, tree sum) and written either as the final output or as a
-//  partial slot for the merge kernel.
+//  LDS (max, rescale, tree sum) and written either as the final output or,
+//  when the head is split over several CTAs, as a partial slot.  The CTA that
+//  arrives last at a split head (one atomic counter per group) merges the
+//  partials by rescaling them to their common max: directly when the head has
+//  at most 16 partials, otherwise through a tree of fan-in 16 whose inner
+//  nodes are written back into partial slots.  No CTA ever waits for another,
+//  so the merge needs no co-residency, and there is no second kernel launch.
 #include "common.h"
 
 namespace attn {
@@ -184,6 +189,157 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
     }
 }
 
+// Partial slots and merge counters are shared between CTAs that may sit on
+// different XCDs, whose L2 caches are not coherent with each other.  Every
+// access to a slot therefore goes through agent-scope atomic loads and stores
+// (relaxed order), which the memory system keeps coherent per location without
+// any L2 writeback or invalidate; a writer waits for its stores to complete
+// (s_waitcnt) before it arrives at the counter, and a reader issues its loads
+// only after its arrival returned.  Agent-scope fences would also be correct,
+// but each one writes back and invalidates a whole L2 and measured several
+// times slower on MI355X.
+// (Whole-vector bit casts only: a bit cast of a single vector element is not
+// reliable with this compiler.)
+__device__ __forceinline__ void st_shared_f4(float *p, const f32x4 &v) {
+    const u64x2 w = __builtin_bit_cast(u64x2, v);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p) + 1, w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 ld_shared_f4(const float *p) {
+    u64x2 w;
+    w[0] = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[1] = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(f32x4, w);
+}
+
+__device__ __forceinline__ void st_shared_f(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float ld_shared_f(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Slot of partial i of a split segment whose pieces sit in CTAs c_lo, c_lo+1, ...
+__device__ __forceinline__ int partial_slot(const LeanPlan &pl, int c_lo, int64_t seg_begin, int i) {
+    return i == 0 ? plan_slot(pl, c_lo, seg_begin) : 2 * (c_lo + i);
+}
+
+// Called by every thread of CTA c right after it wrote its partial of the split
+// segment (b, kh) into its slot (each writing wave has waited for its stores).
+// Arrives at the counter of its merge group; the last arrival merges the group
+// (up to kMergeFanIn states) and either writes the final output (top of the
+// tree) or an inner state into the group's first slot and climbs one level.
+// All control flow is uniform over the CTA.
+template <int HSZ, int NT>
+__device__ void merge_up(const DecodeParams &p, const LeanPiece &pc, int c, int *flag) {
+    const LeanPlan &pl = p.plan;
+    const int G = p.G;
+    const int tid = threadIdx.x;
+    const int nb = (int)(pc.seg_end - pc.seg_begin);
+    const int c_lo = plan_cta_of_tile(pl, pc.seg_begin);
+    const int k = plan_cta_of_tile(pl, pc.seg_begin + nb - 1) - c_lo + 1;  // partials of this head
+    int i = c - c_lo;  // index of the state this CTA carries up the tree
+    int span = 1;      // partials covered by one state at the current level
+    constexpr int UNITS = kMaxGroup * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound
+    for (int level = 0; level < kMergeLevels; ++level) {
+        const MergeGroup mg = plan_merge_group(k, i, span, kMergeFanIn);
+        const int first = mg.first, n = mg.n;
+        const bool top = mg.root;
+        if (n > 1) {
+            __syncthreads();  // every wave's slot stores have completed
+            if (tid == 0) {
+                int *cnt = p.counters + level * 2 * kMaxCtas + partial_slot(pl, c_lo, pc.seg_begin, first * span);
+                const int old = atomicAdd(cnt, 1);
+                const int last = old == n - 1;
+                if (last) atomicExch(cnt, 0);  // counters are zero again for the next call
+                *flag = last;
+            }
+            __syncthreads();
+            if (!*flag) return;
+        } else if (!top) {
+            span *= kMergeFanIn;  // a group of one: its state already sits in place
+            continue;
+        }
+        // merge states first .. first+n-1 of this level
+        const int units = G * HSZ / 4;
+        f32x4 res[UNITS];
+        float Lsum[UNITS], Mmax[UNITS];
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r) {
+            const int u = tid + r * NT;
+            res[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Lsum[r] = 0.f;
+            Mmax[r] = -__builtin_inff();
+            if (u >= units) continue;
+            const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
+            float mv[kMergeFanIn], lv[kMergeFanIn];
+            f32x4 ov[kMergeFanIn];
+#pragma unroll
+            for (int j = 0; j < kMergeFanIn; ++j) {
+                mv[j] = -__builtin_inff();
+                lv[j] = 0.f;
+                ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j < n) {
+                    const float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, (first + j) * span) * p.slot_floats;
+                    mv[j] = ld_shared_f(sp + G * HSZ + g);
+                    lv[j] = ld_shared_f(sp + G * HSZ + G + g);
+                    ov[j] = ld_shared_f4(sp + g * HSZ + 4 * d4);
+                }
+            }
+            float M = mv[0];
+#pragma unroll
+            for (int j = 1; j < kMergeFanIn; ++j) M = fmaxf(M, mv[j]);
+            float L = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMergeFanIn; ++j) {
+                const float f = j < n ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;  // every state is non-empty
+                L += lv[j] * f;
+                O += ov[j] * f;
+            }
+            res[r] = O;
+            Lsum[r] = L;
+            Mmax[r] = M;
+        }
+        if (top) {
+#pragma unroll
+            for (int r = 0; r < UNITS; ++r) {
+                const int u = tid + r * NT;
+                if (u >= units) continue;
+                const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
+                float *dst = p.out + ((int64_t)pc.b * p.Hq + pc.kh * G + g) * HSZ + 4 * d4;
+                *reinterpret_cast<f32x4 *>(dst) = res[r] * (1.f / Lsum[r]);
+            }
+            return;
+        }
+        __syncthreads();  // every member state is read before the first slot is overwritten
+        float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, first * span) * p.slot_floats;
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r) {
+            const int u = tid + r * NT;
+            if (u >= units) continue;
+            const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
+            st_shared_f4(sp + g * HSZ + 4 * d4, res[r]);
+            if (d4 == 0) {
+                st_shared_f(sp + G * HSZ + g, Mmax[r]);
+                st_shared_f(sp + G * HSZ + G + g, Lsum[r]);
+            }
+        }
+        wait_memory();
+        i = first * span;
+        span *= kMergeFanIn;
+    }
+}
+
 template <int HSZ>
 __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
     using C = DecodeCfg<HSZ>;
@@ -214,6 +370,16 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 8; ++i) sel[h][i] = (__bf16)((8 * grp + i == 16 * h + col) ? 1.0f : 0.0f);
+
+    __shared__ int merge_flag;
+
+    // Requests with an empty context own no tiles: their output rows are zero.
+    for (int b = c; b < pl.B; b += pl.P) {
+        if (pl.seqlen[b] != 0) continue;
+        float *orow = p.out + (int64_t)b * p.Hq * HSZ;
+        for (int e = threadIdx.x; e < p.Hq * HSZ / 4; e += W * 64)
+            reinterpret_cast<f32x4 *>(orow)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     int64_t t = plan_cta_begin(pl, c);
     const int64_t t_end = plan_cta_begin(pl, c + 1);
@@ -295,8 +461,9 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             __syncthreads();
         }
 
+        const bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
         if (wave == 0 && col < G) {
-            if (pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end) {
+            if (whole) {
                 const float inv = 1.f / Lt;
                 float *dst = p.out + ((int64_t)pc.b * p.Hq + h0 + col) * HSZ + 4 * grp;
 #pragma unroll
@@ -305,92 +472,16 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
                 float *slot = p.ws + (int64_t)plan_slot(pl, c, pc.seg_begin) * p.slot_floats;
                 float *dst = slot + col * HSZ + 4 * grp;
 #pragma unroll
-                for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db];
+                for (int db = 0; db < ND; ++db) st_shared_f4(dst + 16 * db, oacc[db]);
                 if (grp == 0) {
-                    slot[G * HSZ + col] = M;
-                    slot[G * HSZ + G + col] = Lt;
+                    st_shared_f(slot + G * HSZ + col, M);
+                    st_shared_f(slot + G * HSZ + G + col, Lt);
                 }
             }
+            if (!whole) wait_memory();
         }
+        if (!whole) merge_up<HSZ, W * 64>(p, pc, c, &merge_flag);
         t = pc.tile_end;
-    }
-}
-
-// Merge of split heads.  One workgroup per (segment, head of the group,
-// 16-wide d chunk); its 256 threads are 16 partial lanes x 16 d.  Each thread
-// folds the partials i = lane, lane+16, ... into a running (max, sum, O) with
-// the same rescale the tile kernel uses, four partials per round so their
-// loads are in flight together; the 16 lane states are then folded through
-// LDS.  Segments finished inside one CTA are skipped; empty segments
-// (L_b = 0) get zero rows.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeD = 16;
-constexpr int kMergeLanes = kMergeThreads / kMergeD;
-constexpr int kMergeUnroll = 4;
-
-__device__ __forceinline__ void fold_state(float &M, float &L, float &O, float m2, float l2, float o2) {
-    const float Mn = fmaxf(M, m2);
-    if (Mn == -__builtin_inff()) return;  // both empty
-    const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(m2 - Mn);
-    L = L * a + l2 * b;
-    O = O * a + o2 * b;
-    M = Mn;
-}
-
-template <int HSZ>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeParams p) {
-    __shared__ float red_m[kMergeLanes][kMergeD];
-    __shared__ float red_l[kMergeLanes][kMergeD];
-    __shared__ float red_o[kMergeLanes][kMergeD];
-    const LeanPlan &pl = p.plan;
-    const int s = blockIdx.x, g = blockIdx.y, dc = blockIdx.z;
-    const int b = s / pl.KH, kh = s % pl.KH;
-    const int G = p.G;
-    const int tid = threadIdx.x;
-    const int lane = tid / kMergeD, dd = tid % kMergeD;
-    const int d = dc * kMergeD + dd;
-    float *orow = p.out + ((int64_t)b * p.Hq + kh * G + g) * HSZ;
-    const int nb = plan_tiles_per_segment(pl, b);
-    if (nb == 0) {
-        if (lane == 0) orow[d] = 0.f;
-        return;
-    }
-    const int64_t seg_begin = pl.tile_prefix[b] + (int64_t)kh * nb;
-    const int c_lo = plan_cta_of_tile(pl, seg_begin);
-    const int c_hi = plan_cta_of_tile(pl, seg_begin + nb - 1);
-    if (c_lo == c_hi) return;
-    const int k = c_hi - c_lo + 1;
-    const int slot0 = plan_slot(pl, c_lo, seg_begin);
-    const float NEG_INF = -__builtin_inff();
-
-    float M = NEG_INF, L = 0.f, O = 0.f;
-    for (int i0 = lane; i0 < k; i0 += kMergeLanes * kMergeUnroll) {
-        float mv[kMergeUnroll], lv[kMergeUnroll], ov[kMergeUnroll];
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const int i = i0 + u * kMergeLanes;
-            mv[u] = NEG_INF;
-            lv[u] = 0.f;
-            ov[u] = 0.f;
-            if (i < k) {
-                const int slot = i == 0 ? slot0 : 2 * (c_lo + i);
-                const float *sp = p.ws + (int64_t)slot * p.slot_floats;
-                mv[u] = sp[G * HSZ + g];
-                lv[u] = sp[G * HSZ + G + g];
-                ov[u] = sp[g * HSZ + d];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) fold_state(M, L, O, mv[u], lv[u], ov[u]);
-    }
-    red_m[lane][dd] = M;
-    red_l[lane][dd] = L;
-    red_o[lane][dd] = O;
-    __syncthreads();
-    if (lane == 0) {
-#pragma unroll
-        for (int j = 1; j < kMergeLanes; ++j) fold_state(M, L, O, red_m[j][dd], red_l[j][dd], red_o[j][dd]);
-        orow[d] = O / L;
     }
 }
 
@@ -419,13 +510,6 @@ hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(decode_tiles_kernel<HSZ>, dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds, stream, p);
-    return hipGetLastError();
-}
-
-template <int HSZ>
-hipError_t launch_merge_t(const DecodeParams &p, hipStream_t stream) {
-    dim3 grid(p.plan.B * p.plan.KH, p.G, HSZ / kMergeD);
-    hipLaunchKernelGGL(decode_merge_kernel<HSZ>, grid, dim3(kMergeThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -461,13 +545,19 @@ hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t strea
     }
 }
 
-hipError_t launch_decode_merge(const DecodeParams &p, int Hsz, hipStream_t stream) {
-    switch (Hsz) {
-        case 64: return launch_merge_t<64>(p, stream);
-        case 128: return launch_merge_t<128>(p, stream);
-        case 256: return launch_merge_t<256>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
+// Zero-fills `bytes` (a multiple of 4) with plain vector stores; used for the
+// arrival counters of a freshly allocated workspace.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint32_t *>(ptr), n);
+    return hipGetLastError();
 }
 
 int decode_tiles_occupancy(int Hsz, int G) {

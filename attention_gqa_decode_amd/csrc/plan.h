@@ -94,3 +94,26 @@ ATTN_HD LeanPiece plan_piece_at(const LeanPlan &p, int64_t t, int64_t cta_end) {
 ATTN_HD int plan_slot(const LeanPlan &p, int c, int64_t seg_begin) {
     return 2 * c + (seg_begin <= plan_cta_begin(p, c) ? 0 : 1);
 }
+
+// Merge tree over the k partials of one split segment (partial i comes from
+// CTA c_lo + i).  At a level where one state covers `span` partials there are
+// ceil(k / span) states; state s belongs to the group of states
+// [first, first + n) with first = s rounded down to a multiple of fan_in.  The
+// last member to arrive at a group merges it; when the level has at most
+// fan_in states the group is the root and its merge is the final output,
+// otherwise the merged state covers partials [first*span, (first+n)*span) and
+// is stored in the slot of partial first*span.
+struct MergeGroup {
+    int first;  // first member state of the group (state units of this level)
+    int n;      // members in the group, 1..fan_in
+    bool root;  // the merge of this group is the final output
+};
+
+ATTN_HD MergeGroup plan_merge_group(int k, int i, int span, int fan_in) {
+    MergeGroup g;
+    const int states = (k + span - 1) / span;
+    g.first = (i / span) / fan_in * fan_in;
+    g.n = states - g.first < fan_in ? states - g.first : fan_in;
+    g.root = states <= fan_in;
+    return g;
+}

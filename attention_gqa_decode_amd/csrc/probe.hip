@@ -1,43 +1,69 @@
-// probe.hip -- plain streaming copy of known size (16-byte vector loads and stores).
-// A measurement reference: its bytes are exact, so it calibrates the HBM byte
-// counters and shows the practical streaming rate next to the 8 TB/s peak.
+// probe.hip -- streaming references of known traffic (16-byte non-temporal vector accesses).
+// The copy probe calibrates the HBM byte counters (its bytes are exact); the
+// read probe measures the practical streaming read rate, the ceiling the decode
+// kernel chases.  Both use the access pattern that measured fastest on MI355X:
+// one workgroup of 512 threads per CU, each workgroup streaming its own
+// contiguous slab with four 16-byte loads in flight per thread.
 #include "common.h"
 
 namespace attn {
 namespace {
 
-__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                                         size_t n) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {  // four loads in flight per thread
-        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        dst[i] = a;
-        dst[i + stride] = b;
-        dst[i + 2 * stride] = c;
-        dst[i + 3 * stride] = d;
-    }
-    for (; i < n; i += stride) dst[i] = src[i];
+constexpr int kProbeThreads = 512;
+constexpr int kProbeUnroll = 4;
+
+// Slab of workgroup `blk`: [begin, end) in 16-byte words, a near-equal split of n.
+__device__ __forceinline__ void probe_slab(size_t n, size_t *begin, size_t *end) {
+    *begin = n * blockIdx.x / gridDim.x;
+    *end = n * (blockIdx.x + 1) / gridDim.x;
 }
 
-// Read-only stream: every 16-byte word is loaded once; a per-thread xor is
-// stored only if it matches a value the data never holds, so the kernel
-// writes (almost) nothing and its time is the read rate.
-__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict__ src, size_t n,
-                                                         uint32_t *__restrict__ sink) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    uint32_t acc = 0;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {  // four loads in flight per thread
-        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        const u32x4 w = a ^ b ^ c ^ d;
-        acc ^= w[0] ^ w[1] ^ w[2] ^ w[3];
+__global__ __launch_bounds__(kProbeThreads) void copy_probe_kernel(const u32x4 *__restrict__ src,
+                                                                   u32x4 *__restrict__ dst, size_t n) {
+    size_t i, end;
+    probe_slab(n, &i, &end);
+    constexpr size_t step = (size_t)kProbeUnroll * kProbeThreads;
+    for (i += threadIdx.x; i + (kProbeUnroll - 1) * kProbeThreads < end; i += step) {
+        u32x4 r[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) r[u] = __builtin_nontemporal_load(src + i + u * kProbeThreads);
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) __builtin_nontemporal_store(r[u], dst + i + u * kProbeThreads);
     }
-    for (; i < n; i += stride) {
+    for (; i < end; i += kProbeThreads) dst[i] = src[i];
+}
+
+// Every 16-byte word is loaded once; a per-thread xor is stored only if it
+// matches a value the data never holds, so the kernel writes (almost) nothing.
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4 *__restrict__ src, size_t n,
+                                                                   uint32_t *__restrict__ sink) {
+    size_t i, end;
+    probe_slab(n, &i, &end);
+    constexpr size_t step = (size_t)kProbeUnroll * kProbeThreads;
+    uint32_t acc = 0;
+    for (i += threadIdx.x; i + (kProbeUnroll - 1) * kProbeThreads < end; i += step) {
+        u32x4 r[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) r[u] = __builtin_nontemporal_load(src + i + u * kProbeThreads);
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) acc ^= r[u][0] ^ r[u][1] ^ r[u][2] ^ r[u][3];
+    }
+    for (; i < end; i += kProbeThreads) {
         const u32x4 w = src[i];
         acc ^= w[0] ^ w[1] ^ w[2] ^ w[3];
     }
     if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+hipError_t probe_grid(size_t n, unsigned *grid) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const size_t want = (n + kProbeThreads - 1) / kProbeThreads;
+    *grid = (unsigned)(want < (size_t)cus ? want : (size_t)cus);
+    return hipSuccess;
 }
 
 }  // namespace
@@ -45,32 +71,22 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict
 hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t stream) {
     const size_t n = bytes / 16;
     if (n == 0) return hipSuccess;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
+    unsigned grid = 0;
+    hipError_t e = probe_grid(n, &grid);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    size_t blocks = (n + 255) / 256;
-    const size_t cap = (size_t)cus * 16;
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const u32x4 *>(src), n, static_cast<uint32_t *>(sink));
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(kProbeThreads), 0, stream, static_cast<const u32x4 *>(src),
+                       n, static_cast<uint32_t *>(sink));
     return hipGetLastError();
 }
 
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t stream) {
     const size_t n = bytes / 16;
     if (n == 0) return hipSuccess;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
+    unsigned grid = 0;
+    hipError_t e = probe_grid(n, &grid);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    size_t blocks = (n + 255) / 256;
-    const size_t cap = (size_t)cus * 16;
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
+    hipLaunchKernelGGL(copy_probe_kernel, dim3(grid), dim3(kProbeThreads), 0, stream, static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), n);
     return hipGetLastError();
 }
 

@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the GQA decode/prefill library on one MI355X.
 
-A step is one ``attn_decode`` call (plan, LeanTile kernel, merge kernel) on the
-Llama-3-8B-shaped decode workload: B=16, Hq=32, KH=8 (G=4), Hsz=128, every request
-at 8192 cached tokens, bf16 K/V ~ N(0,1), fp32 output.  ``value`` is the achieved HBM
-bandwidth in algorithmic bytes (every cached K and V byte, the query and the output,
-each counted once) per second of step time, measured with the inputs already resident
-in HBM.  The K/V caches are rotated over enough copies that each step reads bytes the
-256 MiB last-level cache does not hold from the previous step.
+A step is one ``attn_decode_ex`` call (host plan + one decode kernel, whose last CTA per
+split head merges the partial states) on the Llama-3-8B-shaped decode workload: B=16,
+Hq=32, KH=8 (G=4), Hsz=128, every request at 8192 cached tokens, bf16 K/V ~ N(0,1), fp32
+output (``--workload`` picks another decode workload for the headline).  ``value`` is
+the achieved HBM bandwidth in algorithmic bytes (every cached K and V byte, the query
+and the output, each counted once) per second of step time over back-to-back steps,
+with the inputs already resident in HBM.  The K/V caches are rotated over enough
+copies that each step reads bytes the 256 MiB last-level cache does not hold from the
+previous step.
 
-The same run also times: the tile kernel alone (HIP events recorded on the launch
-stream around it -> the ``roofline`` object), the long-context MQA decode (x1 and x8
-scores), the ragged batch, causal prefill (bf16/fp16 MFMA TFLOP/s), a plain copy of
-known size (the practical streaming ceiling), and the fp64 CPU oracle on the headline
-workload (``cpu_baseline``).  One JSON line goes to stdout.
+The same run also times: the decode kernel alone (HIP events recorded on the launch
+stream around each launch -> the ``roofline`` object), the other decode workloads
+(long-context MQA with x1 and x8 scores, the ragged batch), causal prefill (MFMA
+TFLOP/s), a copy and a read of known size (the practical streaming ceiling), and the
+fp64 CPU oracle on the headline workload (``cpu_baseline``).  One JSON line goes to
+stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -88,6 +91,8 @@ def log(msg: str) -> None:
 
 
 def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True):
+    """Times `steps` decode steps back to back (value), then the same number again with HIP
+    events recorded on the launch stream around every decode-kernel launch (roofline)."""
     import torch
 
     import attention_gqa_decode_amd as A
@@ -102,19 +107,25 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     vs = [v] + [v.clone() for _ in range(copies - 1)]
     out = torch.empty((shape.B, shape.Hq, shape.Hsz), dtype=torch.float32, device="cuda")
     scale = shape.score_mult / math.sqrt(shape.Hsz) if shape.score_mult != 1.0 else 0.0
+    calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale) for i in range(copies)]
+    stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
-        A.attn_decode_ex(q, ks[i % copies], vs[i % copies], sl, out=out, scale=scale)
+        calls[i % copies](stream)
     torch.cuda.synchronize()
-    evs = [(hev.create(), hev.create()) for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        A.attn_decode_ex(q, ks[i % copies], vs[i % copies], sl, out=out, scale=scale,
-                         ev_tiles_begin=evs[i][0], ev_tiles_end=evs[i][1])
+        calls[i % copies](stream)
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
+    evs = [(hev.create(), hev.create()) for _ in range(steps)]
+    for i in range(steps):
+        c = calls[i % copies]
+        c.set_events(*evs[i])
+        c(stream)
+        c.set_events(None, None)
+    torch.cuda.synchronize()
     kern = [hev.elapsed_ms(a, b) for a, b in evs]
     for a, b in evs:
         hev.destroy(a)
@@ -126,10 +137,10 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
         "sum_kvsl": int(sum(sl)), "max_kvsl": int(max(sl)), "score_mult": shape.score_mult,
         "kv_copies_rotated": copies, "bytes_per_step": nbytes,
         "us_per_step": step_ms * 1e3, "GBps": nbytes / (step_ms * 1e-3) / 1e9,
-        "tile_kernel_us": kern_ms * 1e3, "tile_kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9,
+        "kernel_us": kern_ms * 1e3, "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9,
     }
     res["frac_of_peak"] = res["GBps"] / PEAK_HBM_GBPS
-    del q, ks, vs, out
+    del q, ks, vs, out, calls
     torch.cuda.empty_cache()
     return res
 
@@ -230,6 +241,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--headline-only", action="store_true", help="time only the headline decode workload")
+    ap.add_argument("--workload", default="llama3_8b",
+                    help="decode workload of the headline line (llama3_8b, long_mqa, long_mqa_x8, ragged, tiny)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -247,15 +260,15 @@ def main():
     cus, lds = A.attn_device_info()
     log(f"device: {torch.cuda.get_device_name(0)}, {cus} CUs, {lds} B LDS/CU")
 
-    head = W.decode_workload("llama3_8b")
-    log("decode llama3_8b ...")
+    head = W.decode_workload(args.workload)
+    log(f"decode {head.name} ...")
     r = bench_decode(head, args.steps, args.warmup, hev)
-    log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, tile kernel {r['tile_kernel_us']:.1f} us")
+    log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, kernel {r['kernel_us']:.1f} us")
     others = []
     probe = None
     prefill = None
     if not args.headline_only:
-        for name in ["long_mqa", "long_mqa_x8", "ragged"]:
+        for name in [n for n in ["llama3_8b", "long_mqa", "long_mqa_x8", "ragged"] if n != head.name]:
             log(f"decode {name} ...")
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
@@ -271,7 +284,7 @@ def main():
         cpu = cpu_baseline(head)
         log(f"  {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
 
-    traffic = committed_traffic("decode_tiles_llama3_8b", r["bytes_per_step"])
+    traffic = committed_traffic(f"decode_{head.name}", r["bytes_per_step"])
     line = {
         "metric": "decode attn achieved HBM GB/s (% peak) + us/step; prefill MFMA TFLOP/s",
         "value": round(r["GBps"], 1),
@@ -285,14 +298,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama3_8b_gqa_decode", "B": head.B, "Hq": head.Hq, "KH": head.KH, "Hsz": head.Hsz,
-                   "kvsl": head.seqlens[0], "out_dtype": "fp32", "parallelism": "single_gpu"},
+        "config": {"workload": f"{head.name}_gqa_decode", "B": head.B, "Hq": head.Hq, "KH": head.KH, "Hsz": head.Hsz,
+                   "kvsl": head.seqlens[0] if len(set(head.seqlens)) == 1 else "ragged",
+                   "sum_kvsl": int(sum(head.seqlens)), "out_dtype": "fp32", "parallelism": "single_gpu"},
         "frac_of_peak_hbm": round(r["frac_of_peak"], 4),
         "us_per_step": round(r["us_per_step"], 2),
-        "roofline": {"bound": "hbm", "achieved": round(r["tile_kernel_GBps"], 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(r["tile_kernel_GBps"] / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode_tiles_kernel<128>",
-                     "kernel_us": round(r["tile_kernel_us"], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(r["kernel_GBps"], 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(r["kernel_GBps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": f"decode_tiles_kernel<{head.Hsz}>",
+                     "kernel_us": round(r["kernel_us"], 2)},
         "cpu_baseline": cpu,
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],

@@ -60,6 +60,10 @@ enum attn_status {
 #define ATTN_MAX_BATCH 256
 /* Largest group size G = Hq / KH the decode kernel holds in one workgroup. */
 #define ATTN_MAX_GROUP 16
+/* Largest number of persistent decode workgroups (num_ctas). */
+#define ATTN_MAX_CTAS 4096
+/* Bytes at the start of a decode workspace that hold the merge counters. */
+#define ATTN_DECODE_COUNTER_BYTES 98304
 
 /*
  * attn_decode -- one decode step of GQA attention (query length 1).
@@ -76,9 +80,11 @@ enum attn_status {
  * The context of every (request, kv head) is cut into LeanTiles of T keys; the
  * tiles of the whole batch are numbered globally and split evenly over all
  * resident workgroups, each of which keeps the G query heads of a group
- * together.  Heads split across workgroups leave partial (max, sum, O) states
- * that a second kernel merges.  The library owns the partial-state buffer
- * (one per device and stream, grown on demand with hipMalloc, freed by
+ * together.  A head split across workgroups leaves one partial (max, sum, O)
+ * state per workgroup; the workgroup that finishes last merges them by
+ * rescaling to the common max, inside the same kernel (one launch per call).
+ * The library owns the partial-state buffer (one per device and stream, grown
+ * on demand with hipMalloc and zero-filled on the stream, freed by
  * attn_release); calls on the same stream are ordered, calls that share a
  * stream from several host threads at once are not supported.
  */
@@ -95,21 +101,27 @@ typedef struct attn_decode_args {
     int B, Hq, KH, Hsz;
     int64_t kv_stride;        /* cache capacity S per (b, kv head); 0 = max_b L_b */
     float scale;              /* softmax scale; <= 0 selects 1/sqrt(Hsz) */
-    void *workspace;          /* optional device buffer for partial states (NULL = library-owned) */
+    void *workspace;          /* optional device buffer for partial states (NULL = library-owned);
+                                 its first ATTN_DECODE_COUNTER_BYTES bytes must be zero before its
+                                 first use, and every completed call leaves them zero again.  One
+                                 workspace serves one call at a time: calls that may overlap
+                                 (different streams) need different workspaces. */
     size_t workspace_bytes;   /* its size; must be >= attn_decode_workspace_bytes(...) */
     int tile_keys;            /* LeanTile size T in keys; 0 = library default */
-    int num_ctas;             /* number of persistent workgroups P; 0 = all resident slots */
-    hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the tile kernel */
-    hipEvent_t ev_tiles_end;  /* optional: recorded right after the tile kernel */
+    int num_ctas;             /* number of persistent workgroups P, <= ATTN_MAX_CTAS;
+                                 0 = all resident slots */
+    hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the decode kernel */
+    hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel */
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
 
 /*
- * Bytes of partial-state workspace attn_decode_ex needs for these sizes when
- * it runs with `num_ctas` workgroups (0 = the library's default for the
- * current device; that query initialises the HIP runtime).  Returns 0 for
- * unsupported sizes.
+ * Bytes of workspace attn_decode_ex needs for these sizes when it runs with
+ * `num_ctas` workgroups (0 = the library's default for the current device;
+ * that query initialises the HIP runtime): ATTN_DECODE_COUNTER_BYTES of merge
+ * counters, then 2 partial slots per workgroup of (G*Hsz + 2G) floats rounded
+ * up to 16 bytes.  Returns 0 for unsupported sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas);
 

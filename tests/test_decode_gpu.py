@@ -119,13 +119,48 @@ def test_gqa_equals_mha_with_repeated_kv():
 def test_caller_workspace_matches_library_workspace():
     q, k, v, sl = inputs(2, 8, 2, 128, [4096, 999], seed=9)
     need = A.attn_decode_workspace_bytes(2, 8, 2, 128, 64)
-    ws = torch.empty(need // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(need // 4, dtype=torch.float32, device="cuda")
     a = gpu_decode(q, k, v, sl, num_ctas=64, workspace=ws)
     b = gpu_decode(q, k, v, sl, num_ctas=64)
     np.testing.assert_array_equal(a, b)
+    counters = ws[: A.ATTN_DECODE_COUNTER_BYTES // 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0, "merge counters must be left at zero"
     with pytest.raises(A.AttnError) as e:
         A.attn_decode_ex(q, k, v, sl, num_ctas=64, workspace=ws[:16])
     assert e.value.status == A.ATTN_ERR_WORKSPACE
+
+
+def test_one_workspace_across_cta_counts():
+    # the counter region sits at a fixed offset, so slots written with one P never alias
+    # the counters of a later call with another P
+    note("decode one caller workspace, P = 64, 700, 64, 3")
+    q, k, v, sl = inputs(2, 8, 2, 128, [5000, 777], seed=13)
+    need = A.attn_decode_workspace_bytes(2, 8, 2, 128, 700)
+    ws = torch.zeros(need // 4, dtype=torch.float32, device="cuda")
+    ref = oracle_decode(q, k, v, sl, 2, 1 / math.sqrt(128))
+    for P in [64, 700, 64, 3]:
+        got = gpu_decode(q, k, v, sl, tile_keys=16, num_ctas=P, workspace=ws)
+        assert np.abs(got - ref).max() <= DECODE_TOL, P
+
+
+@pytest.mark.parametrize("P", [17, 300, 4096])
+def test_deep_merge_trees(P):
+    # one head split over P CTAs: one, two and three levels of the fan-in-16 merge tree
+    L = 16 * P + 5
+    note(f"decode merge tree: L={L}, T=16, P={P}")
+    q, k, v, sl = inputs(1, 8, 1, 128, [L], seed=14 + P)
+    err, got = decode_err(q, k, v, sl, tile_keys=16, num_ctas=P)
+    note(f"  max err {err:.3e}")
+    assert err <= DECODE_TOL
+    again = gpu_decode(q, k, v, sl, tile_keys=16, num_ctas=P)
+    np.testing.assert_array_equal(got, again)  # fixed tree and member order: bitwise repeatable
+
+
+def test_repeated_calls_are_bitwise_identical():
+    q, k, v, sl = inputs(4, 32, 8, 128, [3000, 9000, 1, 4500], seed=15)
+    outs = [gpu_decode(q, k, v, sl) for _ in range(4)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
 
 
 def test_simple_entry_matches_ex():

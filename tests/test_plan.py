@@ -27,6 +27,9 @@ def harness(tmp_path_factory):
     lib.harness_pieces.restype = ctypes.c_int64
     lib.harness_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p, ctypes.c_int64]
+    lib.harness_merge_tree.restype = ctypes.c_int
+    lib.harness_merge_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
     lib.harness_merge_slots.restype = ctypes.c_int
     lib.harness_merge_slots.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
@@ -124,3 +127,35 @@ def test_library_planner_matches_header(harness):
     for c in range(P):
         mine = rows[rows[:, 0] == c]
         assert mine[0, 3] == cta[c] and mine[-1, 4] == cta[c + 1]
+
+
+# ------------------------------------------------------------- fused merge tree
+
+MERGE_FAN_IN, MERGE_LEVELS, MAX_CTAS = 16, 3, 4096  # the kernel's tree shape
+
+
+def merge_tree(harness, k, order):
+    order = np.ascontiguousarray(order, dtype=np.int32)
+    cov = np.zeros(k, dtype=np.int32)
+    left = ctypes.c_int64()
+    roots = harness.harness_merge_tree(k, MERGE_FAN_IN, MERGE_LEVELS, order.ctypes.data, cov.ctypes.data,
+                                       ctypes.byref(left))
+    return roots, cov, left.value
+
+
+@pytest.mark.parametrize("k", [2, 3, 15, 16, 17, 31, 255, 256, 257, 1000, 4095, 4096])
+def test_merge_tree_covers_every_partial_once(harness, k):
+    """Whatever order the CTAs of a split head finish in, exactly one of them produces the
+    output, it folds in every partial exactly once, and every counter is back at zero."""
+    rng = np.random.default_rng(k)
+    for trial in range(3):
+        order = np.arange(k) if trial == 0 else (np.arange(k)[::-1] if trial == 1 else rng.permutation(k))
+        roots, cov, left = merge_tree(harness, k, order)
+        assert roots == 1
+        assert np.all(cov == 1)
+        assert left == 0
+
+
+def test_merge_tree_depth_bound():
+    # kMaxCtas partials of one head need exactly kMergeLevels levels of fan-in 16
+    assert MERGE_FAN_IN ** MERGE_LEVELS == MAX_CTAS
