@@ -240,8 +240,7 @@ __device__ __forceinline__ int partial_slot(const LeanPlan &pl, int c_lo, int64_
 // tree) or an inner state into the group's first slot and climbs one level.
 // All control flow is uniform over the CTA.
 template <int HSZ, int NT>
-__device__ void merge_up(const DecodeParams &p, const LeanPiece &pc, int c, int *flag) {
-    const LeanPlan &pl = p.plan;
+__device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPiece &pc, int c, int *flag) {
     const int G = p.G;
     const int tid = threadIdx.x;
     const int nb = (int)(pc.seg_end - pc.seg_begin);
@@ -359,7 +358,6 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     const int col = lane & 15;  // head g (Q, P, O), key row (K, V) or d (V^T)
     const int grp = lane >> 4;  // 8-wide slice of the MFMA contraction
     const int c = blockIdx.x;
-    const LeanPlan &pl = p.plan;
     const int G = p.G;
     const float NEG_INF = -__builtin_inff();
     uint16_t *stage = stages + wave * C::STAGE;
@@ -372,6 +370,20 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         for (int i = 0; i < 8; ++i) sel[h][i] = (__bf16)((8 * grp + i == 16 * h + col) ? 1.0f : 0.0f);
 
     __shared__ int merge_flag;
+    __shared__ int blk_next;  // next unclaimed 32-key block of the current piece
+    // The plan is read many times (piece lookups, merge slots): one copy in LDS
+    // costs a single round of vector loads instead of chains of dependent
+    // scalar loads from the argument segment.
+    __shared__ LeanPlan plan_lds;
+    {
+        constexpr int WORDS = (int)(sizeof(LeanPlan) / sizeof(int));
+        const int *src = reinterpret_cast<const int *>(&p.plan);
+        int *dst = reinterpret_cast<int *>(&plan_lds);
+        for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
+        if (threadIdx.x == 0) blk_next = W;
+        __syncthreads();
+    }
+    const LeanPlan &pl = plan_lds;
 
     // Requests with an empty context own no tiles: their output rows are zero.
     for (int b = c; b < pl.B; b += pl.P) {
@@ -406,28 +418,35 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
 
         const int nblk = (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
         const int klast = pc.key_end - 1;
-        // Each wave owns blocks wave, wave + W, ...; block n + W is loading
-        // while block n is computed out of the wave's LDS stage.  LDS traffic
+        // Block w starts on wave w; every wave claims its next block from an
+        // LDS counter when it starts computing one, so waves whose loads come
+        // back sooner take more blocks and all waves of the CTA finish within
+        // about one block of each other.  The claimed block is loading while
+        // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
         Staged<HSZ> st;
         int blk = wave;
         if (blk < nblk) load_block<HSZ>(st, kbase, vbase, pc.key_begin + blk * kKeysPerBlock, klast, lane);
-        for (; blk < nblk; blk += W) {
+        while (blk < nblk) {
             store_block<HSZ>(st, stage, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (blk + W < nblk)
-                load_block<HSZ>(st, kbase, vbase, pc.key_begin + (blk + W) * kKeysPerBlock, klast, lane);
+            int nxt = 0;
+            if (lane == 0) nxt = atomicAdd(&blk_next, 1);
+            nxt = __builtin_amdgcn_readfirstlane(nxt);
+            if (nxt < nblk) load_block<HSZ>(st, kbase, vbase, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
             process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, klast, col, grp, p.scale_log2,
                                m_run, l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            blk = nxt;
         }
 
         // ---- merge the W wave states of this piece ----
         l_run = wave_sum_over_groups(l_run);
-        __syncthreads();  // LDS of the previous piece is free
+        __syncthreads();  // every wave left the streaming loop: stages and block counter are free
+        if (threadIdx.x == 0) blk_next = W;  // for the next piece (later barriers publish it)
         if (grp == 0) {
             sm_m[wave * 16 + col] = m_run;
             sm_l[wave * 16 + col] = l_run;
@@ -480,7 +499,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             }
             if (!whole) wait_memory();
         }
-        if (!whole) merge_up<HSZ, W * 64>(p, pc, c, &merge_flag);
+        if (!whole) merge_up<HSZ, W * 64>(p, pl, pc, c, &merge_flag);
         t = pc.tile_end;
     }
 }

@@ -38,6 +38,13 @@ def run_and_check(B, ISL, Hq, KH, Hsz, seed, rows=None):
     assert np.all(np.isfinite(g))
     excess = np.abs(g - r) - (2e-3 + bf16_half_ulp(r))
     note(f"  max |err| {np.abs(g - r).max():.3e}, worst excess over bound {excess.max():.3e}")
+    if excess.max() > 0:
+        worst = np.argsort(excess.max(axis=1))[::-1][:8]
+        for j in worst:
+            flat = int(sel[j])
+            bhq, i = divmod(flat, ISL)
+            col = int(excess[j].argmax())
+            note(f"    row {i} of (b, h) {divmod(bhq, Hq)} col {col}: gpu {g[j, col]:.6f} oracle {r[j, col]:.6f}")
     assert excess.max() <= 0, f"max |err| {np.abs(g - r).max():.3e}"
 
 
