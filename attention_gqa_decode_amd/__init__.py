@@ -24,6 +24,9 @@ ATTN_MAX_BATCH = 256
 ATTN_MAX_GROUP = 16
 ATTN_MAX_CTAS = 4096
 ATTN_DECODE_COUNTER_BYTES = 98304
+ATTN_SCHEDULE_AUTO = 0
+ATTN_SCHEDULE_STREAM_K = 1
+ATTN_SCHEDULE_FIXED_SPLIT = 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -44,6 +47,7 @@ class attn_decode_args(ctypes.Structure):
         ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
         ("tile_keys", _I), ("num_ctas", _I),
         ("ev_tiles_begin", _P), ("ev_tiles_end", _P),
+        ("schedule", _I), ("num_splits", _I),
     ]
 
 
@@ -137,7 +141,8 @@ def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
 
 
 def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
-                   workspace=None, ev_tiles_begin=None, ev_tiles_end=None, stream=None):
+                   workspace=None, ev_tiles_begin=None, ev_tiles_end=None, schedule=ATTN_SCHEDULE_AUTO,
+                   num_splits=0, stream=None):
     """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
 
     ``workspace`` is an optional CUDA tensor used as the partial-state buffer; its first
@@ -169,6 +174,7 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
     a.ev_tiles_begin = ev_tiles_begin
     a.ev_tiles_end = ev_tiles_end
+    a.schedule, a.num_splits = int(schedule), int(num_splits)
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
     return out
 
@@ -181,7 +187,8 @@ class PreparedDecode:
     The caller keeps the tensors alive and unchanged in shape while the object is used.
     """
 
-    def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0):
+    def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
+                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0):
         for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
             _bf16_cuda(n, t)
         B, Hq, Hsz = q.shape
@@ -200,6 +207,7 @@ class PreparedDecode:
         a.kv_stride = S
         a.scale = float(scale)
         a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+        a.schedule, a.num_splits = int(schedule), int(num_splits)
         self._args = a
         self._ref = ctypes.byref(a)
         self._fn = lib().attn_decode_ex

@@ -124,7 +124,25 @@ int build_plan(const int32_t *seqlens, int B, int KH, int T, int64_t stride, Lea
     plan->tile_prefix[B] = (int32_t)acc;
     plan->N = acc;
     plan->P = 1;
+    plan->mode = kPlanStreamK;
+    plan->splits = 1;
     return ATTN_OK;
+}
+
+// Splits per segment of the fixed-split schedule when the caller gives none:
+// enough CTAs to fill every resident slot once (the FlashDecoding default),
+// never more than the longest segment's tiles, within the merge-counter range.
+int default_splits(const LeanPlan &p, int resident) {
+    const int segs = p.B * p.KH;
+    int nmax = 0;
+    for (int b = 0; b < p.B; ++b) {
+        const int n = plan_tiles_per_segment(p, b);
+        nmax = n > nmax ? n : nmax;
+    }
+    int S = (resident + segs - 1) / segs;
+    if (S > nmax) S = nmax;
+    if (S > attn::kMaxCtas / segs) S = attn::kMaxCtas / segs;
+    return S < 1 ? 1 : S;
 }
 
 bool any_split_segment(const LeanPlan &p) {
@@ -179,6 +197,15 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (a->kv_stride < 0) return fail(ATTN_ERR_SHAPE, "kv_stride=%lld is negative", (long long)a->kv_stride);
     if (a->tile_keys < 0 || a->num_ctas < 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be >= 0");
     if (a->num_ctas > attn::kMaxCtas) return fail(ATTN_ERR_UNSUPPORTED, "num_ctas=%d exceeds %d", a->num_ctas, attn::kMaxCtas);
+    if (a->schedule < ATTN_SCHEDULE_AUTO || a->schedule > ATTN_SCHEDULE_FIXED_SPLIT)
+        return fail(ATTN_ERR_SHAPE, "schedule=%d is not an ATTN_SCHEDULE_* value", a->schedule);
+    if (a->num_splits < 0) return fail(ATTN_ERR_SHAPE, "num_splits=%d is negative", a->num_splits);
+    if (a->schedule == ATTN_SCHEDULE_FIXED_SPLIT && a->num_ctas != 0)
+        return fail(ATTN_ERR_SHAPE, "num_ctas is set by the fixed-split schedule (B*KH*num_splits); pass 0");
+    if (a->schedule == ATTN_SCHEDULE_FIXED_SPLIT && a->num_splits > 1 &&
+        (int64_t)a->B * a->KH * a->num_splits > attn::kMaxCtas)
+        return fail(ATTN_ERR_UNSUPPORTED, "B*KH*num_splits=%lld exceeds %d", (long long)a->B * a->KH * a->num_splits,
+                    attn::kMaxCtas);
     if (!(a->scale == a->scale) || isinf(a->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
     if (a->workspace && !aligned16(a->workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
 
@@ -210,12 +237,28 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
                     attn::decode_workspace_bytes(P, G, a->Hsz), P);
 
     // ---- argument checks done; HIP calls from here on ----
-    if (P == 0) {
-        st = device_default_ctas(a->Hsz, G, &P);
-        if (st != ATTN_OK) return st;
-        if (P > attn::kMaxCtas) P = attn::kMaxCtas;
+    int resident = 0;
+    st = device_default_ctas(a->Hsz, G, &resident);
+    if (st != ATTN_OK) return st;
+    // The selector (the digest's runtime selection policy: stream-K tiles for
+    // long, few-head or ragged work; no split when the batch alone fills every
+    // resident slot) picks the fixed split with one CTA per segment when there
+    // are at least twice as many segments as resident workgroups, and stream-K
+    // otherwise.
+    int schedule = a->schedule;
+    if (schedule == ATTN_SCHEDULE_AUTO)
+        schedule = (int64_t)a->B * a->KH >= 2LL * resident && a->num_ctas == 0 ? ATTN_SCHEDULE_FIXED_SPLIT
+                                                                              : ATTN_SCHEDULE_STREAM_K;
+    if (schedule == ATTN_SCHEDULE_FIXED_SPLIT) {
+        const int S = a->num_splits > 0 ? a->num_splits
+                      : a->schedule == ATTN_SCHEDULE_AUTO ? 1 : default_splits(p.plan, resident);
+        p.plan.mode = kPlanFixedSplit;
+        p.plan.splits = S;
+        P = a->B * a->KH * S;
+    } else {
+        if (P == 0) P = resident < attn::kMaxCtas ? resident : attn::kMaxCtas;
+        if (P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;  // no empty CTA; one CTA zeroes an all-empty batch
     }
-    if (P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;  // no empty CTA; one CTA zeroes an all-empty batch
     p.plan.P = P;
     p.counters = nullptr;
 

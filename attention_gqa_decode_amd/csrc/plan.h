@@ -22,6 +22,14 @@
 // CTA c_lo's slot is 2*c_lo if the segment starts exactly where c_lo's range
 // starts (then it is c_lo's first piece) and 2*c_lo+1 otherwise; every later
 // CTA holds the segment as its first piece, slot 2c.
+//
+// Fixed split (the FlashDecoding-style baseline of the digest's section
+// "모양이 다른 프리필과 디코드": a fixed number of splits per launch).  Every
+// segment s is cut into S_s = min(S, n_s) chunks of near-equal tile counts,
+// chunk j = local tiles [floor(j n_s / S_s), floor((j+1) n_s / S_s)); CTA
+// c = s*S + j takes chunk j, so P = B*KH*S and CTAs with j >= S_s own nothing.
+// Chunks never cross segments, so every CTA holds at most one piece and the
+// slot and merge rules above apply unchanged.
 #pragma once
 
 #include <stdint.h>
@@ -36,23 +44,51 @@
 #define ATTN_MAX_BATCH 256
 #endif
 
+enum : int { kPlanStreamK = 0, kPlanFixedSplit = 1 };
+
 struct LeanPlan {
     int B;
     int KH;
     int T;      // keys per LeanTile
-    int P;      // CTAs (1 <= P <= N when N > 0)
+    int P;      // CTAs (stream-K: 1 <= P <= N when N > 0; fixed split: B*KH*splits)
     int64_t N;  // total tiles
+    int mode;   // kPlanStreamK or kPlanFixedSplit
+    int splits; // fixed split: CTAs per segment (S)
     int32_t seqlen[ATTN_MAX_BATCH];           // L_b
     int32_t tile_prefix[ATTN_MAX_BATCH + 1];  // tiles before batch b (all its kv heads)
 };
 
-ATTN_HD int64_t plan_cta_begin(const LeanPlan &p, int c) { return (int64_t)c * p.N / p.P; }
-
-// CTA whose range contains tile t: the largest c with floor(cN/P) <= t.
-ATTN_HD int plan_cta_of_tile(const LeanPlan &p, int64_t t) { return (int)(((t + 1) * p.P - 1) / p.N); }
-
 ATTN_HD int plan_tiles_per_segment(const LeanPlan &p, int b) {
     return (p.tile_prefix[b + 1] - p.tile_prefix[b]) / p.KH;
+}
+
+// First tile of CTA c; plan_cta_begin(p, P) == N.
+ATTN_HD int64_t plan_cta_begin(const LeanPlan &p, int c) {
+    if (p.mode == kPlanStreamK) return (int64_t)c * p.N / p.P;
+    const int s = c / p.splits, j = c % p.splits;
+    if (s >= p.B * p.KH) return p.N;
+    const int b = s / p.KH, kh = s % p.KH;
+    const int n = plan_tiles_per_segment(p, b);
+    const int64_t seg_begin = p.tile_prefix[b] + (int64_t)kh * n;
+    const int chunks = n < p.splits ? n : p.splits;
+    if (chunks == 0) return seg_begin;
+    const int jj = j < chunks ? j : chunks;
+    return seg_begin + (int64_t)jj * n / chunks;
+}
+
+ATTN_HD int plan_batch_of_tile(const LeanPlan &p, int64_t t);
+
+// CTA whose range contains tile t (0 <= t < N).
+ATTN_HD int plan_cta_of_tile(const LeanPlan &p, int64_t t) {
+    if (p.mode == kPlanStreamK) return (int)(((t + 1) * p.P - 1) / p.N);  // largest c with floor(cN/P) <= t
+    const int b = plan_batch_of_tile(p, t);
+    const int n = plan_tiles_per_segment(p, b);
+    const int64_t local = t - p.tile_prefix[b];
+    const int kh = (int)(local / n);
+    const int64_t u = local - (int64_t)kh * n;
+    const int chunks = n < p.splits ? n : p.splits;
+    const int j = (int)(((u + 1) * chunks - 1) / n);  // largest j with floor(j n / chunks) <= u
+    return (b * p.KH + kh) * p.splits + j;
 }
 
 // Batch owning tile t (0 <= t < N): the b with tile_prefix[b] <= t < tile_prefix[b+1].

@@ -9,241 +9,254 @@
 //
 // gfx950 mapping.  A workgroup of 4 wave64s owns 128 query rows of one query
 // head (32 rows per wave) and walks the K/V blocks of 64 keys up to the
-// diagonal.  K is staged row-major in LDS; V is staged transposed (V^T[d][key],
-// written as packed key pairs) so that the PV product can read its MFMA
-// operand with two 8-byte LDS reads.  Both products run on
-// v_mfma_f32_16x16x32_bf16 in the transposed form S^T = K Q^T and
-// O^T = V^T P^T: the query row sits on the lane index, so the row max and row
-// sum need only two cross-lane steps, and the lanes holding S^T already hold
-// the P^T operand (same key order trick as the decode kernel).  The second
-// product runs in fp16 (v_mfma_f32_16x16x32_f16): V is converted bf16 -> fp16
-// while it is staged (exact inside fp16's range, |v| < 65504) and P in [0, 1]
-// is rounded to fp16 (2^-11 relative, four times finer than bf16, whose 2^-9
-// weight error alone breaks a 2e-3 bound on rows with few keys).  The running
-// sum l accumulates the same rounded P, so rounding perturbs the weights but
-// not their normalisation.  Blocks are issued longest-first (late query
-// blocks see the most keys).
+// diagonal; two workgroups share a CU (256 VGPRs per lane, 74 KiB of LDS each),
+// so one's softmax overlaps the other's matrix products.
+//  * Staging: each block's K (bf16) and V (converted to fp16, exact inside
+//    fp16's normal range) go through registers into one of two LDS stages
+//    while the other stage is being computed: one barrier per block.  K rows
+//    are padded to 272 bytes (row-parallel 16-byte operand reads hit distinct
+//    banks), V rows to 320 bytes (the transposed reads below hit distinct banks).
+//  * BMM1 in the transposed form S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a
+//    query row sits on lane (l % 32), so the row max and sum need one exchange
+//    with lane l ^ 32; Q^T stays in registers for the whole key loop.
+//  * Online softmax in the log2 domain with a lazily moved reference max: it
+//    moves only when a block's max exceeds it by more than 2^8, so P <= 256
+//    stays inside fp16 and the O/l rescale runs only on the rare blocks that
+//    move it.  P is rounded to fp16 (2^-11 relative) and the running sum adds
+//    the rounded values (v_dot2_f32_f16), so the weights stay normalised exactly.
+//  * BMM2 as O^T = V^T P^T on v_mfma_f32_32x32x16_f16.  V^T comes straight
+//    from the row-major V stage through ds_read_b64_tr_b16 (each read hands a
+//    lane four consecutive keys of one d), and the key order inside every
+//    16-key contraction is chosen so that the lanes holding S^T already hold
+//    the P^T operand: no shuffles and no transposed staging.
+//  * Order: each XCD takes the work of whole kv heads (their K/V then stays in
+//    its L2), and inside it the query blocks go longest first.
 #include "common.h"
 
 namespace attn {
 namespace {
 
-constexpr int PF_BM = 128;   // query rows per workgroup
-constexpr int PF_BN = 64;    // keys per K/V block
-constexpr int PF_WAVES = 4;  // 32 query rows per wave
+constexpr int PF_HSZ = 128;
+constexpr int PF_BM = 128;  // query rows per workgroup
+constexpr int PF_BN = 64;   // keys per K/V block
+constexpr int PF_WAVES = 4;
+constexpr int PF_NT = PF_WAVES * 64;
+constexpr int PF_KP = PF_HSZ + 8;   // K stage row pitch (bf16 elements): 272 B
+constexpr int PF_VP = PF_HSZ + 32;  // V stage row pitch (fp16 elements): 320 B
+constexpr int PF_KSTAGE = PF_BN * PF_KP;  // elements
+constexpr int PF_VSTAGE = PF_BN * PF_VP;
+constexpr int PF_STAGE = PF_KSTAGE + PF_VSTAGE;
+constexpr int PF_CH = PF_HSZ / 8;                  // 16-byte chunks per row
+constexpr int PF_LOADS = PF_BN * PF_CH / PF_NT;    // 16-byte chunks per thread per block (K, and again V)
+constexpr int PF_XCDS = 8;
+constexpr float kLazy = 8.f;  // lazy-rescale threshold in log2 units (weights <= 256)
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ f32x4 mfma_pf(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma_qk(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma_pv(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma_pv(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-    const f16x2 h = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(uint32_t, h);
+// 8 bf16 (one 16-byte chunk) -> 8 fp16, exact for |v| in fp16's normal range.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 &w) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = w[i];
+        const f16x2 h = {(_Float16)__builtin_bit_cast(float, x << 16), (_Float16)__builtin_bit_cast(float, x & 0xffff0000u)};
+        r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
 }
 
-__device__ __forceinline__ float max_over_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+// Four consecutive keys of one d column of the row-major fp16 V stage.  Within
+// each 16-lane block, lane t reads 8 bytes at row key0 + t/4, columns
+// d0 + 4 (t % 4) .. +3; the transposing read then hands lane i the column
+// d0 + i at rows key0 .. key0+3.
+__device__ __forceinline__ i16x4 v_cols(const uint16_t *vstage, int key0, int d0, int t) {
+    const uint16_t *p = vstage + (key0 + (t >> 2)) * PF_VP + d0 + 4 * (t & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
 }
 
-__device__ __forceinline__ float sum_over_groups(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
-}
-
-template <int HSZ>
-__global__ __launch_bounds__(PF_WAVES * 64) void prefill_causal_kernel(
+__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, int B, int ISL, int Hq, int KH, float scale_log2, int nqb) {
-    constexpr int NS = HSZ / 32;
-    constexpr int ND = HSZ / 16;
-    constexpr int KSTR = HSZ + 8;    // bf16 per K row in LDS (16-byte aligned rows)
-    constexpr int VSTR = PF_BN + 4;  // bf16 per V^T row in LDS (8-byte aligned rows)
-    constexpr int KCH = HSZ / 8;     // 16-byte chunks per row
-    constexpr int NT = PF_WAVES * 64;
-    constexpr int KLOADS = PF_BN * KCH / NT;        // K chunks per thread per block
-    constexpr int VLOADS = (PF_BN / 2) * KCH / NT;  // V key-pair chunks per thread per block
-    __shared__ __attribute__((aligned(16))) uint16_t sk[PF_BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t svt[HSZ * VSTR];  // fp16 V^T
-
+    extern __shared__ __attribute__((aligned(16))) uint16_t pf_smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int nbh = B * Hq;
-    const int qb = nqb - 1 - (int)(blockIdx.x / nbh);  // longest first
-    const int bh = (int)(blockIdx.x % nbh);
-    const int b = bh / Hq, h = bh % Hq;
-    const int kh = h / (Hq / KH);
+    const int l32 = lane & 31, h = lane >> 5;  // query column of the 32x32 tiles, lane half
+    const int G = Hq / KH;
+
+    // ---- work item: XCD-aware when the (b, kv head) pairs split evenly over the XCDs ----
+    const int x = blockIdx.x;
+    const int npair = B * KH;
+    int pair, g, qb;
+    if (npair % PF_XCDS == 0) {
+        const int xcd = x % PF_XCDS, rank = x / PF_XCDS, per = npair / PF_XCDS;
+        g = rank % G;
+        const int rest = rank / G;
+        pair = (rest % per) * PF_XCDS + xcd;
+        qb = nqb - 1 - rest / per;
+    } else {
+        g = x % G;
+        const int rest = x / G;
+        pair = rest % npair;
+        qb = nqb - 1 - rest / npair;
+    }
+    const int b = pair / KH, kh = pair % KH;
+    const int hq = kh * G + g;
+
+    const int64_t bh = (int64_t)b * Hq + hq;
+    const uint16_t *qh = q + bh * ISL * PF_HSZ;
+    const uint16_t *kbase = k + ((int64_t)b * KH + kh) * ISL * PF_HSZ;
+    const uint16_t *vbase = v + ((int64_t)b * KH + kh) * ISL * PF_HSZ;
+    const int q0 = qb * PF_BM + 32 * wave;  // first query row of this wave
     const float NEG_INF = -__builtin_inff();
 
-    const int row0 = qb * PF_BM + 32 * wave;
-    const uint16_t *qh = q + (int64_t)bh * ISL * HSZ;
-    const uint16_t *kbase = k + ((int64_t)b * KH + kh) * ISL * HSZ;
-    const uint16_t *vbase = v + ((int64_t)b * KH + kh) * ISL * HSZ;
-
-    bf16x8 qop[2][NS];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        int row = row0 + 16 * rb + col;
+    // Q^T operands: lane holds query q0 + l32, d = 16s + 8h .. +7.
+    bf16x8 qop[PF_HSZ / 16];
+    {
+        int row = q0 + l32;
         row = row < ISL ? row : ISL - 1;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            qop[rb][s] = *reinterpret_cast<const bf16x8 *>(qh + (int64_t)row * HSZ + 32 * s + 8 * grp);
+        for (int s = 0; s < PF_HSZ / 16; ++s)
+            qop[s] = *reinterpret_cast<const bf16x8 *>(qh + (int64_t)row * PF_HSZ + 16 * s + 8 * h);
     }
 
-    float m[2] = {NEG_INF, NEG_INF};
-    float l[2] = {0.f, 0.f};
-    f32x4 oacc[2][ND];
+    f32x16 oacc[PF_HSZ / 32];  // O^T[d = 32dt + 8(r/4) + 4h + r%4][query l32]
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < PF_HSZ / 32; ++dt) oacc[dt] = f32x16{};
+    float m_run = NEG_INF, l_run = 0.f;
 
     int last_key = qb * PF_BM + PF_BM - 1;
     last_key = last_key < ISL - 1 ? last_key : ISL - 1;
     const int nkv = last_key / PF_BN + 1;
 
-    u32x4 kst[KLOADS], vst[VLOADS][2];
+    u32x4 kst[PF_LOADS], vst[PF_LOADS];
     auto load_block = [&](int kvb) {
-        const int kb0 = kvb * PF_BN;
 #pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int idx = r * NT + tid;
-            int key = kb0 + idx / KCH;
+        for (int r = 0; r < PF_LOADS; ++r) {
+            const int idx = r * PF_NT + tid;
+            int key = kvb * PF_BN + idx / PF_CH;
             key = key < ISL ? key : ISL - 1;
-            kst[r] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * HSZ + 8 * (idx % KCH));
-        }
-#pragma unroll
-        for (int r = 0; r < VLOADS; ++r) {
-            const int idx = r * NT + tid;
-            const int pr = idx / KCH, ch = idx % KCH;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                int key = kb0 + 2 * pr + e;
-                key = key < ISL ? key : ISL - 1;
-                vst[r][e] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * HSZ + 8 * ch);
-            }
+            const int64_t off = (int64_t)key * PF_HSZ + 8 * (idx % PF_CH);
+            kst[r] = *reinterpret_cast<const u32x4 *>(kbase + off);
+            vst[r] = *reinterpret_cast<const u32x4 *>(vbase + off);
         }
     };
-    auto store_block = [&]() {
+    auto store_block = [&](int stage) {
+        uint16_t *ks = pf_smem + stage * PF_STAGE;
+        uint16_t *vs = ks + PF_KSTAGE;
 #pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int idx = r * NT + tid;
-            *reinterpret_cast<u32x4 *>(sk + (idx / KCH) * KSTR + 8 * (idx % KCH)) = kst[r];
-        }
-#pragma unroll
-        for (int r = 0; r < VLOADS; ++r) {
-            const int idx = r * NT + tid;
-            const int pr = idx / KCH, ch = idx % KCH;
-            uint32_t *dst = reinterpret_cast<uint32_t *>(svt) + ((8 * ch) * VSTR + 2 * pr) / 2;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = vst[r][0][w], c = vst[r][1][w];
-                // d = 8ch + 2w (low halves) and 8ch + 2w + 1 (high halves); keys 2pr, 2pr+1.
-                // bf16 -> fp32 is exact; fp32 -> fp16 is exact for |v| in fp16's normal range.
-                dst[(2 * w) * VSTR / 2] = pack_f16(bf16_lo(a), bf16_lo(c));
-                dst[(2 * w + 1) * VSTR / 2] = pack_f16(bf16_hi(a), bf16_hi(c));
-            }
+        for (int r = 0; r < PF_LOADS; ++r) {
+            const int idx = r * PF_NT + tid;
+            const int row = idx / PF_CH, ch = idx % PF_CH;
+            *reinterpret_cast<u32x4 *>(ks + row * PF_KP + 8 * ch) = kst[r];
+            *reinterpret_cast<u32x4 *>(vs + row * PF_VP + 8 * ch) = bf16x8_to_f16x8(vst[r]);
         }
     };
 
     load_block(0);
+    store_block(0);
+    __syncthreads();
     for (int kvb = 0; kvb < nkv; ++kvb) {
-        __syncthreads();
-        store_block();
-        __syncthreads();
+        const int stage = kvb & 1;
         if (kvb + 1 < nkv) load_block(kvb + 1);
         const int key_base = kvb * PF_BN;
-        if (key_base > row0 + 31) continue;  // block entirely above this wave's diagonal
-
-        f32x4 sc[4][2];
+        if (key_base <= q0 + 31) {  // some key of the block is visible to some row of this wave
+            const uint16_t *ks = pf_smem + stage * PF_STAGE;
+            const uint16_t *vs = ks + PF_KSTAGE;
+            // ---- BMM1: S^T[key = 32kt + 8(r/4) + 4h + r%4][query l32] ----
+            f32x16 sc[2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+            for (int kt = 0; kt < 2; ++kt) {
+                sc[kt] = f32x16{};
+                const uint16_t *krow = ks + (32 * kt + l32) * PF_KP + 8 * h;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sk + (16 * kb + col) * KSTR + 32 * s + 8 * grp);
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_pf(a, qop[rb][s], sc[kb][rb]);
+                for (int s = 0; s < PF_HSZ / 16; ++s)
+                    sc[kt] = mfma_qk(*reinterpret_cast<const bf16x8 *>(krow + 16 * s), qop[s], sc[kt]);
             }
-
-        const bool diag = key_base + PF_BN - 1 > row0;  // some key of the block lies past some row
-        f16x8 pb[2][2];
+            // ---- online softmax (log2 domain, lazy rescale) ----
+            const int row = q0 + l32;
+            const bool diag = key_base + PF_BN - 1 > q0;
+            float mx = NEG_INF;  // max raw score of this query over the block
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int row = row0 + 16 * rb + col;
-            float x[16];
-            float mx = NEG_INF;
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = key_base + 16 * kb + 4 * grp + i;
-                    float xv = sc[kb][rb][i] * scale_log2;
-                    if (diag && key > row) xv = NEG_INF;
-                    x[4 * kb + i] = xv;
-                    mx = fmaxf(mx, xv);
+                for (int r = 0; r < 16; ++r) {
+                    if (diag && key_base + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3) > row) sc[kt][r] = NEG_INF;
+                    mx = fmaxf(mx, sc[kt][r]);
                 }
-            mx = max_over_groups(mx);
-            const float m_new = fmaxf(m[rb], mx);
-            const float m_use = m_new == NEG_INF ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_use);
-            float ps = 0.f;
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+            // The reference max moves only when the block max exceeds it by more
+            // than kLazy (log2 units): the weights then stay <= 2^kLazy, far inside
+            // fp16, and O and l are rescaled only on the rare blocks that move it.
+            // Any reference value gives the same softmax, so this is exact up to rounding.
+            const bool move = mx > m_run + kLazy;  // always true on the first block (m_run = -inf)
+            const float m_new = move ? mx : m_run;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const _Float16 pr = (_Float16)__builtin_amdgcn_exp2f(x[j] - m_use);
-                ps += (float)pr;
-                // k-slot order inside a 32-key chunk kc: slots 0-3 <- 16-key block 2kc, 4-7 <- 2kc+1
-                const int kb = j >> 2, i = j & 3;
-                pb[rb][kb >> 1][4 * (kb & 1) + i] = pr;
+                for (int dt = 0; dt < PF_HSZ / 32; ++dt) oacc[dt] *= alpha;
             }
-            l[rb] = l[rb] * alpha + ps;
-            m[rb] = m_new;
+            m_run = m_new;
+            f16x8 pb[4];  // P^T operands of the four 16-key chunks
+            const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[rb][db] *= alpha;
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pb[c][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + e], scale_log2, -m_new));
+                // the running sum adds the fp16-rounded weights the product uses
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const f16x2 pair = {pb[c][e], pb[c][e + 1]};
+                    l_run = __builtin_amdgcn_fdot2(pair, ones, l_run, false);
+                }
+            }
+            // ---- BMM2: O^T += V^T P^T; contraction slot 8h + e of chunk c is key
+            //      16c + 4h + e (e < 4) or 16c + 8 + 4h + (e - 4) (e >= 4) ----
+            const int t = lane & 15;
+#pragma unroll
+            for (int dt = 0; dt < PF_HSZ / 32; ++dt) {
+                const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const i16x4 lo = v_cols(vs, 16 * c + 4 * h, d0, t);
+                    const i16x4 hi = v_cols(vs, 16 * c + 8 + 4 * h, d0, t);
+                    const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[dt] = mfma_pv(a, pb[c], oacc[dt]);
+                }
+            }
         }
-
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                const uint16_t *vrow = svt + (16 * db + col) * VSTR + 32 * kc + 4 * grp;
-                const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow);
-                const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + 16);
-                const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) oacc[rb][db] = mfma_pv(a, pb[rb][kc], oacc[rb][db]);
-            }
+        if (kvb + 1 < nkv) store_block(stage ^ 1);
+        __syncthreads();
     }
 
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float lt = sum_over_groups(l[rb]);
-        const int row = row0 + 16 * rb + col;
-        if (row >= ISL) continue;
+    // ---- epilogue: O = O^T / l, rounded to bf16 once ----
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    const int row = q0 + l32;
+    if (row < ISL) {
         const float inv = 1.f / lt;
-        uint16_t *orow = out + ((int64_t)bh * ISL + row) * HSZ + 4 * grp;
+        uint16_t *orow = out + (bh * ISL + row) * PF_HSZ;
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            bf16x4 o;
+        for (int dt = 0; dt < PF_HSZ / 32; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[rb][db][i] * inv);
-            *reinterpret_cast<bf16x4 *>(orow + 16 * db) = o;
-        }
+            for (int m4 = 0; m4 < 4; ++m4) {
+                bf16x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[dt][4 * m4 + i] * inv);
+                *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * m4 + 4 * h) = o;
+            }
     }
 }
 
@@ -252,12 +265,20 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefill_causal_kernel(
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                                  int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
                                  hipStream_t stream) {
-    if (Hsz != 128) return hipErrorInvalidValue;
+    if (Hsz != PF_HSZ) return hipErrorInvalidValue;
     const int nqb = (ISL + PF_BM - 1) / PF_BM;
     const int64_t nblocks = (int64_t)nqb * B * Hq;
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_causal_kernel<128>, dim3((unsigned)nblocks), dim3(PF_WAVES * 64), 0, stream,
-                       q, k, v, out, B, ISL, Hq, KH, scale_log2, nqb);
+    const size_t lds = (size_t)2 * PF_STAGE * sizeof(uint16_t);
+    static bool attr_set = false;  // above the default dynamic-LDS limit (gfx950 has 160 KiB per CU)
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_causal_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(prefill_causal_kernel, dim3((unsigned)nblocks), dim3(PF_NT), lds, stream, q, k, v, out, B, ISL,
+                       Hq, KH, scale_log2, nqb);
     return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True):
+def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
     events recorded on the launch stream around every decode-kernel launch (roofline)."""
     import torch
@@ -107,7 +107,7 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     vs = [v] + [v.clone() for _ in range(copies - 1)]
     out = torch.empty((shape.B, shape.Hq, shape.Hsz), dtype=torch.float32, device="cuda")
     scale = shape.score_mult / math.sqrt(shape.Hsz) if shape.score_mult != 1.0 else 0.0
-    calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale) for i in range(copies)]
+    calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale, schedule=schedule) for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         calls[i % copies](stream)
@@ -265,6 +265,7 @@ def main():
     r = bench_decode(head, args.steps, args.warmup, hev)
     log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, kernel {r['kernel_us']:.1f} us")
     others = []
+    schedules = []
     probe = None
     prefill = None
     if not args.headline_only:
@@ -273,6 +274,15 @@ def main():
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
             others.append(o)
+        log("schedules: stream-K vs fixed split ...")
+        for name in ["llama3_8b", "long_mqa", "ragged"]:
+            shp = W.decode_workload(name)
+            sk = bench_decode(shp, args.steps, args.warmup, hev, schedule=A.ATTN_SCHEDULE_STREAM_K)
+            fs = bench_decode(shp, args.steps, args.warmup, hev, schedule=A.ATTN_SCHEDULE_FIXED_SPLIT)
+            schedules.append({"workload": name, "stream_k_us": round(sk["us_per_step"], 2),
+                              "fixed_split_us": round(fs["us_per_step"], 2),
+                              "fixed_split_over_stream_k": round(fs["us_per_step"] / sk["us_per_step"], 3)})
+            log(f"  {name}: stream-K {sk['us_per_step']:.1f} us, fixed split {fs['us_per_step']:.1f} us")
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
@@ -310,6 +320,7 @@ def main():
         "cpu_baseline": cpu,
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],
+        "schedules": schedules,
         "prefill": prefill,
         "hbm_probes": probe,
     }

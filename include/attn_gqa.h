@@ -91,6 +91,28 @@ enum attn_status {
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
                 int B, int Hq, int KH, int Hsz, float *out, hipStream_t stream);
 
+/*
+ * Work schedules of the decode kernel (attn_decode_args.schedule).
+ *   ATTN_SCHEDULE_STREAM_K    LeanTiles numbered over the whole batch and split
+ *                             evenly over num_ctas persistent workgroups (the
+ *                             LeanAttention digest, "조각별로 합칠 수 있는 정확한
+ *                             소프트맥스" and "하드웨어에 맞춘 작업 단위").
+ *   ATTN_SCHEDULE_FIXED_SPLIT every (request, kv head) context cut into
+ *                             num_splits near-equal chunks, one workgroup each
+ *                             (the FlashDecoding-style baseline the digest compares
+ *                             against, section "모양이 다른 프리필과 디코드");
+ *                             num_splits = 0 fills every resident slot once.
+ *   ATTN_SCHEDULE_AUTO        the selector: one workgroup per (request, kv head)
+ *                             when there are at least twice as many of them as
+ *                             resident workgroups (the batch fills the GPU, no
+ *                             reduction needed), stream-K otherwise (section
+ *                             "런타임 선택 정책").
+ * All schedules compute the same function; results differ only by fp32 rounding.
+ */
+#define ATTN_SCHEDULE_AUTO 0
+#define ATTN_SCHEDULE_STREAM_K 1
+#define ATTN_SCHEDULE_FIXED_SPLIT 2
+
 /* Full-control decode.  Fields not listed keep the attn_decode meaning. */
 typedef struct attn_decode_args {
     const void *q;            /* bf16 [B][Hq][Hsz] */
@@ -108,10 +130,13 @@ typedef struct attn_decode_args {
                                  (different streams) need different workspaces. */
     size_t workspace_bytes;   /* its size; must be >= attn_decode_workspace_bytes(...) */
     int tile_keys;            /* LeanTile size T in keys; 0 = library default */
-    int num_ctas;             /* number of persistent workgroups P, <= ATTN_MAX_CTAS;
-                                 0 = all resident slots */
+    int num_ctas;             /* stream-K: number of persistent workgroups P, <= ATTN_MAX_CTAS;
+                                 0 = all resident slots.  Must be 0 for the fixed split. */
     hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the decode kernel */
     hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel */
+    int schedule;             /* ATTN_SCHEDULE_*; 0 = AUTO */
+    int num_splits;           /* fixed split: chunks per (request, kv head); 0 = fill the GPU once.
+                                 With more than one split, B*KH*num_splits <= ATTN_MAX_CTAS. */
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);

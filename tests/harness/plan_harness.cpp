@@ -11,8 +11,8 @@
 
 extern "C" {
 
-// rows of 8 int64: cta, b, kh, tile_begin, tile_end, key_begin, key_end, slot (-1 = whole segment)
-int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int64_t *rows, int64_t max_rows) {
+// Plan as the library builds it; splits > 0 selects the fixed split (P = B*KH*splits).
+static LeanPlan make_plan(const int32_t *seqlens, int B, int KH, int T, int P, int splits) {
     LeanPlan p;
     p.B = B;
     p.KH = KH;
@@ -25,7 +25,17 @@ int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int6
     }
     p.tile_prefix[B] = (int32_t)acc;
     p.N = acc;
-    p.P = P;
+    p.mode = splits > 0 ? kPlanFixedSplit : kPlanStreamK;
+    p.splits = splits > 0 ? splits : 1;
+    p.P = splits > 0 ? B * KH * splits : P;
+    return p;
+}
+
+// rows of 8 int64: cta, b, kh, tile_begin, tile_end, key_begin, key_end, slot (-1 = whole segment)
+int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int splits, int64_t *rows,
+                       int64_t max_rows) {
+    LeanPlan p = make_plan(seqlens, B, KH, T, P, splits);
+    P = p.P;
     int64_t n = 0;
     for (int c = 0; c < P; ++c) {
         int64_t t = plan_cta_begin(p, c), te = plan_cta_begin(p, c + 1);
@@ -46,20 +56,9 @@ int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int6
 
 // For segment s = b*KH + kh: writes the slots the merge kernel reads, returns their count
 // (0 when the segment is finished by one CTA or is empty).
-int harness_merge_slots(const int32_t *seqlens, int B, int KH, int T, int P, int s, int32_t *slots, int max_slots) {
-    LeanPlan p;
-    p.B = B;
-    p.KH = KH;
-    p.T = T;
-    int64_t acc = 0;
-    for (int b = 0; b < B; ++b) {
-        p.seqlen[b] = seqlens[b];
-        p.tile_prefix[b] = (int32_t)acc;
-        acc += (int64_t)KH * ((seqlens[b] + (int64_t)T - 1) / T);
-    }
-    p.tile_prefix[B] = (int32_t)acc;
-    p.N = acc;
-    p.P = P;
+int harness_merge_slots(const int32_t *seqlens, int B, int KH, int T, int P, int splits, int s, int32_t *slots,
+                        int max_slots) {
+    LeanPlan p = make_plan(seqlens, B, KH, T, P, splits);
     int b = s / KH, kh = s % KH;
     int nb = plan_tiles_per_segment(p, b);
     if (nb == 0) return 0;

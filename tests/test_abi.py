@@ -102,6 +102,11 @@ def ex_args(**kw):
     (dict(workspace=FAKE, workspace_bytes=16, num_ctas=4), A.ATTN_ERR_WORKSPACE),
     (dict(workspace=FAKE, workspace_bytes=98304, num_ctas=4), A.ATTN_ERR_WORKSPACE),  # counters only
     (dict(num_ctas=4097), A.ATTN_ERR_UNSUPPORTED),
+    (dict(schedule=3), A.ATTN_ERR_SHAPE),
+    (dict(schedule=-1), A.ATTN_ERR_SHAPE),
+    (dict(num_splits=-2), A.ATTN_ERR_SHAPE),
+    (dict(schedule=2, num_ctas=16), A.ATTN_ERR_SHAPE),       # the fixed split sets P itself
+    (dict(schedule=2, num_splits=2000), A.ATTN_ERR_UNSUPPORTED),  # B*KH*splits > ATTN_MAX_CTAS
 ])
 def test_decode_ex_rejects_bad_arguments(kw, status):
     a, _sl = ex_args(**kw)

@@ -205,3 +205,45 @@ def test_ragged_sweep_points(G, Hsz):
     assert err <= DECODE_TOL
     del q, k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ schedules
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 7, 64])
+def test_fixed_split_schedule(splits):
+    # FlashDecoding-style baseline: every (request, kv head) context cut into `splits`
+    # chunks (0 = fill the GPU once); ragged lengths, empty and one-key contexts included
+    note(f"decode fixed split S={splits}")
+    q, k, v, sl = inputs(5, 16, 4, 128, [3000, 0, 1, 700, 5555], seed=20 + splits)
+    err, got = decode_err(q, k, v, sl, schedule=A.ATTN_SCHEDULE_FIXED_SPLIT, num_splits=splits)
+    note(f"  max err {err:.3e}")
+    assert err <= DECODE_TOL
+    assert np.all(got[1] == 0)
+    base = gpu_decode(q, k, v, sl, schedule=A.ATTN_SCHEDULE_STREAM_K)
+    assert np.abs(got - base).max() <= 1e-5
+
+
+def test_auto_schedule_many_segments():
+    # 256 requests x 8 kv heads: at least twice the resident workgroups, so the selector
+    # runs one workgroup per (request, kv head) with no reduction
+    rng = np.random.default_rng(21)
+    sl = rng.integers(1, 400, 256).tolist()
+    note(f"decode auto schedule, B=256 KH=8, sum(L)={sum(sl)}")
+    q, k, v, sl = inputs(256, 32, 8, 64, sl, seed=21)
+    rows = np.random.default_rng(22).choice(256 * 32, 200, replace=False)
+    err, got = decode_err(q, k, v, sl, rows=rows)
+    assert err <= DECODE_TOL
+    sk = gpu_decode(q, k, v, sl, schedule=A.ATTN_SCHEDULE_STREAM_K)
+    assert np.abs(got - sk).max() <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["long_mqa", "ragged"])
+def test_fixed_split_full_size(name):
+    s = W.decode_workload(name)
+    note(f"decode fixed split full-size {name}")
+    q, k, v, sl = W.decode_inputs(s, device="cuda")
+    err, _ = decode_err(q, k, v, sl.tolist(), scale_mult=s.score_mult, schedule=A.ATTN_SCHEDULE_FIXED_SPLIT)
+    note(f"  max err {err:.3e}")
+    assert err <= DECODE_TOL
+    del q, k, v
+    torch.cuda.empty_cache()

@@ -26,28 +26,28 @@ def harness(tmp_path_factory):
     lib = ctypes.CDLL(str(out))
     lib.harness_pieces.restype = ctypes.c_int64
     lib.harness_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_void_p, ctypes.c_int64]
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
     lib.harness_merge_tree.restype = ctypes.c_int
     lib.harness_merge_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
     lib.harness_merge_slots.restype = ctypes.c_int
     lib.harness_merge_slots.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
     return lib
 
 
-def pieces(harness, sl, KH, T, P):
+def pieces(harness, sl, KH, T, P, splits=0):
     sl = np.ascontiguousarray(sl, dtype=np.int32)
-    n = harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, None, 0)
+    n = harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, splits, None, 0)
     rows = np.zeros((max(n, 1), 8), dtype=np.int64)
-    harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, rows.ctypes.data, n)
+    harness.harness_pieces(sl.ctypes.data, len(sl), KH, T, P, splits, rows.ctypes.data, n)
     return rows[:n]
 
 
-def merge_slots(harness, sl, KH, T, P, s):
+def merge_slots(harness, sl, KH, T, P, s, splits=0):
     sl = np.ascontiguousarray(sl, dtype=np.int32)
     buf = np.zeros(4 * P + 4, dtype=np.int32)
-    k = harness.harness_merge_slots(sl.ctypes.data, len(sl), KH, T, P, s, buf.ctypes.data, len(buf))
+    k = harness.harness_merge_slots(sl.ctypes.data, len(sl), KH, T, P, splits, s, buf.ctypes.data, len(buf))
     return buf[:k].tolist()
 
 
@@ -68,10 +68,13 @@ CASES = [
 
 
 @pytest.mark.parametrize("sl,KH,T,P", CASES)
-def test_every_key_covered_once_and_slots_consistent(harness, sl, KH, T, P):
+def test_every_key_covered_once_and_slots_consistent(harness, sl, KH, T, P, splits=0):
     N = total_tiles(sl, KH, T)
-    P = min(P, N) if N else 1
-    rows = pieces(harness, sl, KH, T, P)
+    if splits:
+        P = len(sl) * KH * splits
+    else:
+        P = min(P, N) if N else 1
+    rows = pieces(harness, sl, KH, T, P, splits)
     cover = {}
     per_cta_tiles = np.zeros(P, dtype=np.int64)
     written = {}
@@ -92,15 +95,27 @@ def test_every_key_covered_once_and_slots_consistent(harness, sl, KH, T, P):
             assert segs[0][0] == 0 and segs[-1][1] == L
             for (a0, a1), (b0, b1) in zip(segs, segs[1:]):
                 assert a1 == b0, "gap or overlap between pieces"
-            expect = merge_slots(harness, sl, KH, T, P, b * KH + kh)
+            expect = merge_slots(harness, sl, KH, T, P, b * KH + kh, splits)
             got = sorted(s for s, seg in written.items() if seg == (b, kh))
             if len(segs) == 1:
                 assert expect == [] and got == []
             else:
                 assert sorted(expect) == got
     if N:
-        assert per_cta_tiles.max() - per_cta_tiles.min() <= 1
         assert per_cta_tiles.sum() == N
+        if splits:
+            # fixed split: CTA s*S + j holds chunk j of segment s, chunks within a tile of each other
+            for b, L in enumerate(sl):
+                n = (L + T - 1) // T
+                for kh in range(KH):
+                    loads = per_cta_tiles[(b * KH + kh) * splits:(b * KH + kh + 1) * splits]
+                    assert loads.sum() == n
+                    chunks = min(n, splits)
+                    assert np.all(loads[chunks:] == 0)
+                    if chunks:
+                        assert loads[:chunks].max() - loads[:chunks].min() <= 1 and loads[:chunks].min() >= 1
+        else:
+            assert per_cta_tiles.max() - per_cta_tiles.min() <= 1
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -113,6 +128,30 @@ def test_random_plans(harness, seed):
     T = int(rng.choice([1, 16, 32, 48, 100, 256, 1024]))
     P = int(rng.integers(1, 600))
     test_every_key_covered_once_and_slots_consistent(harness, sl.tolist(), KH, T, P)
+
+
+@pytest.mark.parametrize("sl,KH,T,splits", [
+    ([1024], 2, 256, 4),
+    ([8192] * 16, 8, 256, 2),
+    ([262144], 1, 256, 256),
+    ([0, 1, 5, 0, 300, 17], 3, 16, 7),
+    ([518, 64654, 3000, 777], 8, 100, 13),
+    ([33, 31, 0], 2, 1024, 1),
+])
+def test_fixed_split_covers_every_key_once(harness, sl, KH, T, splits):
+    test_every_key_covered_once_and_slots_consistent(harness, sl, KH, T, 0, splits=splits)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fixed_split_plans(harness, seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 30))
+    KH = int(rng.integers(1, 9))
+    sl = rng.integers(0, 5000, B)
+    sl[rng.random(B) < 0.2] = 0
+    T = int(rng.choice([1, 16, 32, 100, 256]))
+    splits = int(rng.integers(1, max(2, 4096 // (B * KH))))
+    test_every_key_covered_once_and_slots_consistent(harness, sl.tolist(), KH, T, 0, splits=splits)
 
 
 def test_library_planner_matches_header(harness):
