@@ -61,6 +61,11 @@ def _load():
     lib.oracle_prefill_causal_f64.argtypes = [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_double, _P, _I64, _P]
     lib.oracle_prefill_causal_f64.restype = ctypes.c_int
+    lib.oracle_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_decode_fp8_f64.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          _I64, ctypes.c_double, ctypes.c_double, ctypes.c_double, _P, _I64, _P]
+    lib.oracle_decode_fp8_f64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -163,3 +168,39 @@ def prefill_causal(q, k, v, KH: int, scale: float, rows=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_prefill_causal_f64 rejected its arguments")
     return out
+
+
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Exact OCP E4M3 (e4m3fn) decode of uint8 codes to float64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    f = _load().oracle_fp8_e4m3_to_f64
+    return np.array([f(int(c)) for c in codes.ravel()], dtype=np.float64).reshape(codes.shape)
+
+
+def decode_fp8(q, k, v, seqlens, Hq: int, KH: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+               rows=None) -> np.ndarray:
+    """Decode attention over an E4M3 KV cache.
+
+    q: uint16 bf16 bits [B][Hq][Hsz]; k, v: uint8 E4M3 codes [B][KH][S][Hsz]; the attended
+    key is k_scale * K and the value v_scale * V.  Returns float64 [B][Hq][Hsz] (NaN rows
+    when ``rows`` leaves them out).
+    """
+    q = _u16(q)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    v = np.ascontiguousarray(v, dtype=np.uint8)
+    B, Hq_, Hsz = q.shape
+    assert Hq_ == Hq and k.shape[0] == B and k.shape[1] == KH and k.shape[3] == Hsz and v.shape == k.shape
+    S = k.shape[2]
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    out = np.full((B, Hq, Hsz), np.nan)
+    if rows is None:
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rp, nr = _ptr(rows), rows.size
+    rc = _load().oracle_decode_fp8_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), B, Hq, KH, Hsz, S, float(scale),
+                                       float(k_scale), float(v_scale), rp, nr, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode_fp8_f64 rejected its arguments")
+    return out
+

@@ -33,12 +33,20 @@
  * every score, exponential, sum and quotient is fp64.  Two passes per output
  * row (max, then weights), no online update, no tiling.
  *
+ *  - FP8 KV cache (co-design page, TL;DR and checklist "체크리스트": shrink
+ *    the KV state; FP8 is named among the compression options): K and V are
+ *    stored as OCP 8-bit floats E4M3 (1 sign, 4 exponent bits with bias 7, 3
+ *    mantissa bits, exponent field 0 = subnormals, S.1111.111 = NaN, no
+ *    infinity) with one scale per tensor: the attended key is k_scale * K and
+ *    the value v_scale * V.  Decoded exactly to double.
+ *
  * Pins (tests/test_oracle.py): closed forms for one and two keys, q = 0 gives
  * the mean of V, constant V, V = identity gives the weights (rows sum to 1,
  * matched to scipy's softmax), key permutation and common key shift
  * invariance, a planted score near 200, merge of arbitrary splits, GQA equal
  * to MHA with repeated K/V, torch CPU scaled_dot_product_attention in fp64,
- * and prefill row 0 = v_0.
+ * prefill row 0 = v_0; the E4M3 decoder on all 256 codes against torch's
+ * float8_e4m3fn, and the FP8 decode against the bf16 decode on the same values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -207,3 +215,64 @@ int oracle_prefill_causal_f64(const uint16_t *q, const uint16_t *k, const uint16
     }
     return 0;
 }
+
+/* OCP E4M3 (e4m3fn) code -> double, exactly. */
+double oracle_fp8_e4m3_to_f64(uint8_t code) {
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);          /* subnormal: m/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7); /* normal: 1.m * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/*
+ * Decode attention over an FP8 E4M3 KV cache.  q [B][Hq][Hsz] bf16 bits;
+ * k, v [B][KH][S][Hsz] E4M3 codes; key j of head kh is k_scale * decode(k),
+ * value v_scale * decode(v).  Same two passes as oracle_decode_f64, on the
+ * decoded values.  rows: optional list of flat (b*Hq + h) indices (NULL = all).
+ */
+int oracle_decode_fp8_f64(const uint16_t *q, const uint8_t *k, const uint8_t *v,
+                          const int32_t *seqlens, int B, int Hq, int KH, int Hsz, int64_t S,
+                          double scale, double k_scale, double v_scale,
+                          const int64_t *rows, int64_t nrows, double *out) {
+    if (!q || !k || !v || !seqlens || !out || !dims_ok(B, Hq, KH, Hsz) || S < 0) return -1;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] > S) return -1;
+    int G = Hq / KH;
+    int64_t total = rows ? nrows : (int64_t)B * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < total; ++r) {
+        int64_t bh = rows ? rows[r] : r;
+        int b = (int)(bh / Hq), h = (int)(bh % Hq);
+        int kh = h / G;
+        int64_t L = seqlens[b];
+        const uint8_t *kb = k + ((int64_t)b * KH + kh) * S * Hsz;
+        const uint8_t *vb = v + ((int64_t)b * KH + kh) * S * Hsz;
+        const uint16_t *qrow = q + bh * Hsz;
+        double *dst = out + bh * Hsz;
+        for (int d = 0; d < Hsz; ++d) dst[d] = 0.0;
+        if (L == 0) continue;
+        double *sc = (double *)malloc((size_t)L * sizeof(double));
+        double m = -INFINITY;
+        for (int64_t j = 0; j < L; ++j) {
+            double acc = 0.0;
+            for (int d = 0; d < Hsz; ++d)
+                acc += oracle_bf16_to_f64(qrow[d]) * (k_scale * oracle_fp8_e4m3_to_f64(kb[j * Hsz + d]));
+            sc[j] = scale * acc;
+            if (sc[j] > m) m = sc[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            double w = exp(sc[j] - m);
+            l += w;
+            for (int d = 0; d < Hsz; ++d) dst[d] += w * (v_scale * oracle_fp8_e4m3_to_f64(vb[j * Hsz + d]));
+        }
+        for (int d = 0; d < Hsz; ++d) dst[d] /= l;
+        free(sc);
+    }
+    return 0;
+}
+

@@ -339,3 +339,67 @@ def test_decimal_brute_force_tiny(oracle):
     for d in range(Hsz):
         exact = sum(w[j] * D(float(vf[j, d])) for j in range(L)) / tot
         assert abs(float(exact) - out[0, 0, d]) < 1e-14
+
+
+# ------------------------------------------------------------ FP8 E4M3 KV cache
+
+def test_fp8_e4m3_known_codes(oracle):
+    # OCP E4M3: bias 7, 3 mantissa bits, exponent field 0 = subnormals, S.1111.111 = NaN
+    cases = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x30: 0.5, 0xB8: -1.0, 0xC4: -3.0}
+    for code, val in cases.items():
+        assert oracle.fp8_e4m3_to_f64([code])[0] == val, hex(code)
+    assert np.isnan(oracle.fp8_e4m3_to_f64([0x7F])[0]) and np.isnan(oracle.fp8_e4m3_to_f64([0xFF])[0])
+    neg0 = oracle.fp8_e4m3_to_f64([0x80])[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+
+
+def test_fp8_e4m3_all_codes_match_torch(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def fp8_codes(x) -> np.ndarray:
+    """float array -> E4M3 codes via torch's round-to-nearest-even, saturating conversion."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def fp8_as_bf16_bits(codes) -> np.ndarray:
+    """E4M3 codes -> the bf16 bit patterns of the same values (exact: E4M3 fits bf16)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.5, 4.0), (0.0625, 0.25)])
+def test_fp8_decode_equals_bf16_decode_of_the_same_values(oracle, k_scale, v_scale):
+    # every E4M3 value is a bf16 value, and power-of-two scales are exact: the FP8 oracle
+    # must reproduce the pinned bf16 oracle with the scale folded into q.k and out
+    rng = np.random.default_rng(30)
+    B, Hq, KH, Hsz, S = 2, 8, 2, 64, 90
+    sl = [90, 37]
+    q = rand_bits(rng, (B, Hq, Hsz))
+    k8, v8 = fp8_codes(rng.standard_normal((B, KH, S, Hsz)) * 3), fp8_codes(rng.standard_normal((B, KH, S, Hsz)))
+    got = oracle.decode_fp8(q, k8, v8, sl, Hq, KH, 0.125, k_scale, v_scale)
+    ref = oracle.decode(q, fp8_as_bf16_bits(k8), fp8_as_bf16_bits(v8), sl, Hq, KH, 0.125 * k_scale) * v_scale
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_fp8_decode_closed_forms(oracle):
+    rng = np.random.default_rng(31)
+    Hsz = 64
+    q = rand_bits(rng, (1, 4, Hsz))
+    k8 = fp8_codes(rng.standard_normal((1, 1, 5, Hsz)))
+    v8 = fp8_codes(rng.standard_normal((1, 1, 5, Hsz)))
+    # one key: the scaled value itself
+    out = oracle.decode_fp8(q, k8, v8, [1], 4, 1, 0.125, 1.0, 0.5)
+    for h in range(4):
+        np.testing.assert_array_equal(out[0, h], 0.5 * oracle.fp8_e4m3_to_f64(v8[0, 0, 0]))
+    # constant V: the constant, whatever the scores
+    vc = np.full((1, 1, 5, Hsz), 0x3C, dtype=np.uint8)  # 1.5
+    out = oracle.decode_fp8(q, k8, vc, [5], 4, 1, 0.125, 3.0, 2.0)
+    np.testing.assert_allclose(out, 3.0, rtol=0, atol=1e-15)

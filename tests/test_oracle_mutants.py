@@ -28,6 +28,12 @@ MUTANTS = {
     "mask_excludes_diagonal": ("0, i + 1, Hsz", "0, i + (i == 0), Hsz"),
     "codec_shift": ("((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
     "transposed_q_index": ("attend_rows(q + bh * Hsz", "attend_rows(q + (bh % Hq) * Hsz"),
+    "fp8_fnuz_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "fp8_no_subnormals": ("v = ldexp((double)m / 8.0, -6);", "v = 0.0;"),
+    "fp8_sign_lost": ("return sign ? -v : v;", "return v;"),
+    "fp8_v_scale_dropped": ("dst[d] += w * (v_scale * oracle_fp8_e4m3_to_f64(vb[j * Hsz + d]));",
+                            "dst[d] += w * oracle_fp8_e4m3_to_f64(vb[j * Hsz + d]);"),
+    "fp8_k_scale_dropped": ("(k_scale * oracle_fp8_e4m3_to_f64(kb[j * Hsz + d]))", "oracle_fp8_e4m3_to_f64(kb[j * Hsz + d])"),
     "prefill_wrong_kv_head": ("const uint16_t *kb = k + ((int64_t)b * KH + kh) * ISL * Hsz;",
                               "const uint16_t *kb = k + ((int64_t)b * KH + (h % KH)) * ISL * Hsz;"),
 }
@@ -45,6 +51,10 @@ PIN_CALLS = [
     (pins.test_decode_matches_torch_sdpa_fp64, {"Hq": 8, "KH": 2, "Hsz": 64}),
     (pins.test_prefill_matches_torch_sdpa_causal_fp64, {}),
     (pins.test_prefill_row0_is_v0_and_rows_match_decode, {}),
+    (pins.test_fp8_e4m3_known_codes, {}),
+    (pins.test_fp8_e4m3_all_codes_match_torch, {}),
+    (pins.test_fp8_decode_equals_bf16_decode_of_the_same_values, {"k_scale": 0.5, "v_scale": 4.0}),
+    (pins.test_fp8_decode_closed_forms, {}),
 ]
 
 
