@@ -27,6 +27,8 @@ ATTN_DECODE_COUNTER_BYTES = 98304
 ATTN_SCHEDULE_AUTO = 0
 ATTN_SCHEDULE_STREAM_K = 1
 ATTN_SCHEDULE_FIXED_SPLIT = 2
+ATTN_KV_BF16 = 0
+ATTN_KV_FP8_E4M3 = 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -48,6 +50,7 @@ class attn_decode_args(ctypes.Structure):
         ("tile_keys", _I), ("num_ctas", _I),
         ("ev_tiles_begin", _P), ("ev_tiles_end", _P),
         ("schedule", _I), ("num_splits", _I),
+        ("kv_dtype", _I), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
 
 
@@ -107,6 +110,18 @@ def _bf16_cuda(name, t):
         raise TypeError(f"{name} must be a contiguous bf16 CUDA tensor (got {t.dtype}, {t.device})")
 
 
+def _kv_cuda(name, t):
+    """K/V cache check: bf16, or FP8 E4M3 (torch.float8_e4m3fn or raw uint8 codes).  Returns kv_dtype."""
+    import torch
+    if not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA tensor (got {t.device})")
+    if t.dtype == torch.bfloat16:
+        return ATTN_KV_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return ATTN_KV_FP8_E4M3
+    raise TypeError(f"{name} must be bf16 or FP8 E4M3 (float8_e4m3fn / uint8 codes), got {t.dtype}")
+
+
 def _host_seqlens(seqlens):
     import numpy as np
     import torch
@@ -142,7 +157,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
 
 def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
                    workspace=None, ev_tiles_begin=None, ev_tiles_end=None, schedule=ATTN_SCHEDULE_AUTO,
-                   num_splits=0, stream=None):
+                   num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
     """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
 
     ``workspace`` is an optional CUDA tensor used as the partial-state buffer; its first
@@ -151,8 +166,10 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     raw ``hipEvent_t`` handles (ints) recorded around the decode kernel.
     """
     import torch
-    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        _bf16_cuda(n, t)
+    _bf16_cuda("q", q)
+    kv_dtype = _kv_cuda("k_cache", k_cache)
+    if _kv_cuda("v_cache", v_cache) != kv_dtype:
+        raise TypeError("k_cache and v_cache must have the same element type")
     B, Hq, Hsz = q.shape
     KH, S = k_cache.shape[1], k_cache.shape[2]
     sl = _host_seqlens(seqlens)
@@ -175,6 +192,7 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     a.ev_tiles_begin = ev_tiles_begin
     a.ev_tiles_end = ev_tiles_end
     a.schedule, a.num_splits = int(schedule), int(num_splits)
+    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
     return out
 
@@ -188,9 +206,11 @@ class PreparedDecode:
     """
 
     def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
-                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0):
-        for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-            _bf16_cuda(n, t)
+                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0):
+        _bf16_cuda("q", q)
+        kv_dtype = _kv_cuda("k_cache", k_cache)
+        if _kv_cuda("v_cache", v_cache) != kv_dtype:
+            raise TypeError("k_cache and v_cache must have the same element type")
         B, Hq, Hsz = q.shape
         KH, S = k_cache.shape[1], k_cache.shape[2]
         self._sl = _host_seqlens(seqlens)
@@ -208,6 +228,7 @@ class PreparedDecode:
         a.scale = float(scale)
         a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
         a.schedule, a.num_splits = int(schedule), int(num_splits)
+        a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
         self._args = a
         self._ref = ctypes.byref(a)
         self._fn = lib().attn_decode_ex

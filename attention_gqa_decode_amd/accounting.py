@@ -14,8 +14,12 @@ def kv_cache_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_pe
     return 2 * layers * kv_heads * head_dim * bytes_per_elem
 
 
-def decode_bytes(seqlens, B: int, Hq: int, KH: int, Hsz: int, in_bytes: int = 2, out_bytes: int = 4) -> int:
-    kv = sum(2 * KH * int(L) * Hsz * in_bytes for L in seqlens)
+def decode_bytes(seqlens, B: int, Hq: int, KH: int, Hsz: int, in_bytes: int = 2, out_bytes: int = 4,
+                 kv_bytes: int | None = None) -> int:
+    """Bytes a decode step must move: K and V of every cached token (kv_bytes per element,
+    default in_bytes), the query (in_bytes) and the output (out_bytes)."""
+    kvb = in_bytes if kv_bytes is None else kv_bytes
+    kv = sum(2 * KH * int(L) * Hsz * kvb for L in seqlens)
     return kv + B * Hq * Hsz * in_bytes + B * Hq * Hsz * out_bytes
 
 

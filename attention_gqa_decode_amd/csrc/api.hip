@@ -200,6 +200,12 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (a->schedule < ATTN_SCHEDULE_AUTO || a->schedule > ATTN_SCHEDULE_FIXED_SPLIT)
         return fail(ATTN_ERR_SHAPE, "schedule=%d is not an ATTN_SCHEDULE_* value", a->schedule);
     if (a->num_splits < 0) return fail(ATTN_ERR_SHAPE, "num_splits=%d is negative", a->num_splits);
+    if (a->kv_dtype != ATTN_KV_BF16 && a->kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_ERR_SHAPE, "kv_dtype=%d is not an ATTN_KV_* value", a->kv_dtype);
+    if (!(a->k_scale == a->k_scale) || isinf(a->k_scale) || !(a->v_scale == a->v_scale) || isinf(a->v_scale))
+        return fail(ATTN_ERR_SHAPE, "k_scale and v_scale must be finite");
+    if (a->kv_dtype == ATTN_KV_BF16 && (a->k_scale > 0.f || a->v_scale > 0.f) && (a->k_scale != 1.f || a->v_scale != 1.f))
+        return fail(ATTN_ERR_SHAPE, "k_scale and v_scale apply to FP8 caches only");
     if (a->schedule == ATTN_SCHEDULE_FIXED_SPLIT && a->num_ctas != 0)
         return fail(ATTN_ERR_SHAPE, "num_ctas is set by the fixed-split schedule (B*KH*num_splits); pass 0");
     if (a->schedule == ATTN_SCHEDULE_FIXED_SPLIT && a->num_splits > 1 &&
@@ -229,7 +235,10 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.G = G;
     p.slot_floats = attn::decode_slot_floats(G, a->Hsz);
     const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Hsz);
-    p.scale_log2 = scale * 1.4426950408889634f;
+    const bool fp8 = a->kv_dtype == ATTN_KV_FP8_E4M3;
+    const float k_scale = fp8 && a->k_scale > 0.f ? a->k_scale : 1.f;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.v_scale = fp8 && a->v_scale > 0.f ? a->v_scale : 1.f;
 
     int P = a->num_ctas;
     if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, G, a->Hsz) > a->workspace_bytes)
@@ -282,7 +291,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     hipError_t e;
     if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
         return fail_hip(e, "hipEventRecord(begin)");
-    e = attn::launch_decode_tiles(p, a->Hsz, stream);
+    e = attn::launch_decode_tiles(p, a->Hsz, fp8, stream);
     if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
     if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
         return fail_hip(e, "hipEventRecord(end)");

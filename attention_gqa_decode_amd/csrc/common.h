@@ -20,8 +20,8 @@ constexpr int kKeysPerBlock = 32;   // keys one wave consumes per step (two 16-k
 // Kernel arguments of the decode tile kernel (passed by value: the plan rides in kernargs).
 struct DecodeParams {
     const uint16_t *q;   // bf16 [B][Hq][Hsz]
-    const uint16_t *k;   // bf16 [B][KH][S][Hsz]
-    const uint16_t *v;   // bf16 [B][KH][S][Hsz]
+    const uint16_t *k;   // [B][KH][S][Hsz], bf16 or (reinterpreted) FP8 E4M3 bytes
+    const uint16_t *v;   // same layout as k
     float *out;          // fp32 [B][Hq][Hsz]
     float *ws;           // partial slots, each slot_floats long
     int *counters;       // arrival counters [kMergeLevels][2 * kMaxCtas], zero between calls
@@ -29,7 +29,8 @@ struct DecodeParams {
     int Hq;
     int G;
     int slot_floats;     // G*Hsz (O) + G (m) + G (l), rounded up to a multiple of 4
-    float scale_log2;    // softmax scale * log2(e)
+    float scale_log2;    // softmax scale * key scale * log2(e)
+    float v_scale;       // value scale (1 for bf16 caches)
     LeanPlan plan;
 };
 
@@ -51,7 +52,7 @@ inline size_t decode_workspace_bytes(int P, int G, int Hsz) {
 }
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream);
+hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int G);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave

@@ -79,40 +79,79 @@ struct DecodeCfg {
 // One wave's next block in registers: fully coalesced 16-byte loads (lane l of
 // load j reads chunk (64j + l) of the block, row-major over keys), marked
 // non-temporal because every byte is used exactly once.  Rows past klast are
-// clamped re-reads of row klast (their scores are masked later).
-template <int HSZ>
-struct Staged {
-    u32x4 r[DecodeCfg<HSZ>::LOADS];
+// clamped re-reads of row klast (their scores are masked later).  An element
+// is 2 bytes (bf16) or 1 byte (FP8 E4M3): a 16-byte chunk holds 8 or 16 of them.
+template <int HSZ, bool FP8>
+struct KvCfg {
+    static constexpr int EPC = FP8 ? 16 : 8;                          // elements per 16-byte chunk
+    static constexpr int CPR = HSZ / EPC;                             // chunks per row
+    static constexpr int LOADS = 2 * kKeysPerBlock * CPR / 64;        // chunks per lane per block (K + V)
 };
 
-template <int HSZ>
-__device__ __forceinline__ void load_block(Staged<HSZ> &st, const uint16_t *kbase, const uint16_t *vbase, int key0,
+template <int HSZ, bool FP8>
+struct Staged {
+    u32x4 r[KvCfg<HSZ, FP8>::LOADS];
+};
+
+template <int HSZ, bool FP8>
+__device__ __forceinline__ void load_block(Staged<HSZ, FP8> &st, const uint8_t *kbase, const uint8_t *vbase, int key0,
                                            int klast, int lane) {
-    using C = DecodeCfg<HSZ>;
-    constexpr int HALF = C::LOADS / 2;
+    using K = KvCfg<HSZ, FP8>;
+    constexpr int HALF = K::LOADS / 2;
+    constexpr int EB = FP8 ? 1 : 2;  // bytes per element
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
         const int c = 64 * j + lane;
-        int key = key0 + c / C::CH;
+        int key = key0 + c / K::CPR;
         key = key < klast ? key : klast;
-        const int64_t off = (int64_t)key * HSZ + 8 * (c % C::CH);
+        const int64_t off = ((int64_t)key * HSZ + K::EPC * (c % K::CPR)) * EB;
         st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off));
         st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vbase + off));
     }
 }
 
-// Registers -> this wave's LDS stage, rows padded by 16 bytes (row-parallel
-// 16-byte reads of the MFMA operands then hit distinct banks).
-template <int HSZ>
-__device__ __forceinline__ void store_block(const Staged<HSZ> &st, uint16_t *stage, int lane) {
+// 16 E4M3 codes -> 16 bf16 (two 16-byte halves), exactly: every E4M3 value is a
+// bf16 value, and the conversion runs with scale 1.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4 &w, u32x4 &lo, u32x4 &hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+        if (i < 2) {
+            lo[2 * i] = a;
+            lo[2 * i + 1] = b;
+        } else {
+            hi[2 * i - 4] = a;
+            hi[2 * i - 3] = b;
+        }
+    }
+}
+
+// Registers -> this wave's LDS stage as bf16, rows padded by 16 bytes
+// (row-parallel 16-byte reads of the MFMA operands then hit distinct banks).
+template <int HSZ, bool FP8>
+__device__ __forceinline__ void store_block(const Staged<HSZ, FP8> &st, uint16_t *stage, int lane) {
     using C = DecodeCfg<HSZ>;
-    constexpr int HALF = C::LOADS / 2;
+    using K = KvCfg<HSZ, FP8>;
+    constexpr int HALF = K::LOADS / 2;
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
         const int c = 64 * j + lane;
-        const int row = c / C::CH, ch = c % C::CH;
-        *reinterpret_cast<u32x4 *>(stage + row * C::RS + 8 * ch) = st.r[j];
-        *reinterpret_cast<u32x4 *>(stage + (kKeysPerBlock + row) * C::RS + 8 * ch) = st.r[HALF + j];
+        const int row = c / K::CPR, col = K::EPC * (c % K::CPR);
+        uint16_t *kd = stage + row * C::RS + col;
+        uint16_t *vd = stage + (kKeysPerBlock + row) * C::RS + col;
+        if constexpr (FP8) {
+            u32x4 a, b;
+            fp8x16_to_bf16(st.r[j], a, b);
+            *reinterpret_cast<u32x4 *>(kd) = a;
+            *reinterpret_cast<u32x4 *>(kd + 8) = b;
+            fp8x16_to_bf16(st.r[HALF + j], a, b);
+            *reinterpret_cast<u32x4 *>(vd) = a;
+            *reinterpret_cast<u32x4 *>(vd + 8) = b;
+        } else {
+            *reinterpret_cast<u32x4 *>(kd) = st.r[j];
+            *reinterpret_cast<u32x4 *>(vd) = st.r[HALF + j];
+        }
     }
 }
 
@@ -316,7 +355,7 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
                 if (u >= units) continue;
                 const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
                 float *dst = p.out + ((int64_t)pc.b * p.Hq + pc.kh * G + g) * HSZ + 4 * d4;
-                *reinterpret_cast<f32x4 *>(dst) = res[r] * (1.f / Lsum[r]);
+                *reinterpret_cast<f32x4 *>(dst) = res[r] * (p.v_scale / Lsum[r]);
             }
             return;
         }
@@ -339,7 +378,7 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
     }
 }
 
-template <int HSZ>
+template <int HSZ, bool FP8>
 __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
     using C = DecodeCfg<HSZ>;
     constexpr int NS = C::NS;
@@ -398,8 +437,8 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     while (t < t_end) {
         const LeanPiece pc = plan_piece_at(pl, t, t_end);
         const int64_t kvrow = ((int64_t)pc.b * pl.KH + pc.kh) * p.kv_stride;
-        const uint16_t *kbase = p.k + kvrow * HSZ;
-        const uint16_t *vbase = p.v + kvrow * HSZ;
+        const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k) + kvrow * HSZ * (FP8 ? 1 : 2);
+        const uint8_t *vbase = reinterpret_cast<const uint8_t *>(p.v) + kvrow * HSZ * (FP8 ? 1 : 2);
         const int h0 = pc.kh * G;
 
         bf16x8 qop[NS];
@@ -424,17 +463,17 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         // about one block of each other.  The claimed block is loading while
         // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
-        Staged<HSZ> st;
+        Staged<HSZ, FP8> st;
         int blk = wave;
-        if (blk < nblk) load_block<HSZ>(st, kbase, vbase, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        if (blk < nblk) load_block<HSZ, FP8>(st, kbase, vbase, pc.key_begin + blk * kKeysPerBlock, klast, lane);
         while (blk < nblk) {
-            store_block<HSZ>(st, stage, lane);
+            store_block<HSZ, FP8>(st, stage, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             int nxt = 0;
             if (lane == 0) nxt = atomicAdd(&blk_next, 1);
             nxt = __builtin_amdgcn_readfirstlane(nxt);
-            if (nxt < nblk) load_block<HSZ>(st, kbase, vbase, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
+            if (nxt < nblk) load_block<HSZ, FP8>(st, kbase, vbase, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
             process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, klast, col, grp, p.scale_log2,
                                m_run, l_run, oacc);
@@ -483,7 +522,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         const bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
         if (wave == 0 && col < G) {
             if (whole) {
-                const float inv = 1.f / Lt;
+                const float inv = p.v_scale / Lt;
                 float *dst = p.out + ((int64_t)pc.b * p.Hq + h0 + col) * HSZ + 4 * grp;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db] * inv;
@@ -520,15 +559,15 @@ size_t tiles_lds_bytes(int Hsz, int G) {
     }
 }
 
-template <int HSZ>
+template <int HSZ, bool FP8>
 hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
     const size_t lds = decode_tiles_lds_bytes<HSZ>(p.G);
     if (lds > 65536) {  // above the default dynamic-LDS limit; gfx950 has 160 KiB per CU
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(decode_tiles_kernel<HSZ>, dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds, stream, p);
+    hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8>), dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -537,9 +576,9 @@ int occupancy_t(int G) {
     int blocks = 0;
     const size_t lds = decode_tiles_lds_bytes<HSZ>(G);
     if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ>, DecodeCfg<HSZ>::W * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false>, DecodeCfg<HSZ>::W * 64,
                                                      decode_tiles_lds_bytes<HSZ>(G)) != hipSuccess)
         return 1;
     return blocks > 0 ? blocks : 1;
@@ -555,11 +594,14 @@ int decode_tile_keys(int Hsz) {
     }
 }
 
-hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, hipStream_t stream) {
-    switch (Hsz) {
-        case 64: return launch_tiles_t<64>(p, stream);
-        case 128: return launch_tiles_t<128>(p, stream);
-        case 256: return launch_tiles_t<256>(p, stream);
+hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream) {
+    switch (Hsz * 2 + (fp8 ? 1 : 0)) {
+        case 128: return launch_tiles_t<64, false>(p, stream);
+        case 129: return launch_tiles_t<64, true>(p, stream);
+        case 256: return launch_tiles_t<128, false>(p, stream);
+        case 257: return launch_tiles_t<128, true>(p, stream);
+        case 512: return launch_tiles_t<256, false>(p, stream);
+        case 513: return launch_tiles_t<256, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

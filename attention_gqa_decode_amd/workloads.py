@@ -139,3 +139,28 @@ def bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> its bit patterns as a numpy uint16 array (copied to host)."""
     assert t.dtype == torch.bfloat16
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def decode_inputs_fp8(shape: DecodeShape, device="cpu", k_scale: float = 1.0, v_scale: float = 1.0, S: int | None = None):
+    """(q bf16, k, v as uint8 OCP E4M3 codes, seqlens): K/V ~ N(0,1) stored as K/k_scale, V/v_scale.
+
+    The codes come from torch's round-to-nearest-even conversion to float8_e4m3fn after
+    clamping to the format's range (|x| <= 448); the attended key is k_scale * code value.
+    """
+    S = shape.S if S is None else S
+    q = randn_bf16((shape.B, shape.Hq, shape.Hsz), shape.seed, device)
+    g = _generator(device, shape.seed + 7919)
+    k = torch.randn((shape.B, shape.KH, S, shape.Hsz), generator=g, dtype=torch.float32, device=device)
+    k = (k / k_scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    g = _generator(device, shape.seed + 15485863)
+    v = torch.randn((shape.B, shape.KH, S, shape.Hsz), generator=g, dtype=torch.float32, device=device)
+    v = (v / v_scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    sl = torch.tensor(shape.seqlens, dtype=torch.int32)
+    return q, k, v, sl
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    """uint8 tensor -> numpy uint8 array (copied to host)."""
+    assert t.dtype == torch.uint8
+    return t.detach().contiguous().cpu().numpy()
+

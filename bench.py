@@ -90,7 +90,8 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0):
+def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0,
+                 fp8: bool = False):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
     events recorded on the launch stream around every decode-kernel launch (roofline)."""
     import torch
@@ -99,9 +100,12 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     from attention_gqa_decode_amd import accounting as acc
     from attention_gqa_decode_amd import workloads as W
 
-    q, k, v, sl = W.decode_inputs(shape, device="cuda")
+    if fp8:
+        q, k, v, sl = W.decode_inputs_fp8(shape, device="cuda")
+    else:
+        q, k, v, sl = W.decode_inputs(shape, device="cuda")
     sl = sl.tolist()
-    kv_read = 2 * shape.KH * sum(sl) * shape.Hsz * 2
+    kv_read = 2 * shape.KH * sum(sl) * shape.Hsz * (1 if fp8 else 2)
     copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(kv_read, 1)))) if rotate else 1
     ks = [k] + [k.clone() for _ in range(copies - 1)]
     vs = [v] + [v.clone() for _ in range(copies - 1)]
@@ -130,10 +134,10 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     for a, b in evs:
         hev.destroy(a)
         hev.destroy(b)
-    nbytes = acc.decode_bytes(sl, shape.B, shape.Hq, shape.KH, shape.Hsz)
+    nbytes = acc.decode_bytes(sl, shape.B, shape.Hq, shape.KH, shape.Hsz, kv_bytes=1 if fp8 else 2)
     kern_ms = sum(kern) / len(kern)
     res = {
-        "workload": shape.name, "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
+        "workload": shape.name + ("_fp8" if fp8 else ""), "kv_dtype": "fp8_e4m3" if fp8 else "bf16", "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
         "sum_kvsl": int(sum(sl)), "max_kvsl": int(max(sl)), "score_mult": shape.score_mult,
         "kv_copies_rotated": copies, "bytes_per_step": nbytes,
         "us_per_step": step_ms * 1e3, "GBps": nbytes / (step_ms * 1e-3) / 1e9,
@@ -272,6 +276,11 @@ def main():
         for name in [n for n in ["llama3_8b", "long_mqa", "long_mqa_x8", "ragged"] if n != head.name]:
             log(f"decode {name} ...")
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
+            log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
+            others.append(o)
+        for name in ["llama3_8b", "long_mqa", "ragged"]:
+            log(f"decode {name} with an FP8 E4M3 KV cache ...")
+            o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev, fp8=True)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
             others.append(o)
         log("schedules: stream-K vs fixed split ...")

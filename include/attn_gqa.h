@@ -113,11 +113,26 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
 #define ATTN_SCHEDULE_STREAM_K 1
 #define ATTN_SCHEDULE_FIXED_SPLIT 2
 
+/*
+ * Element types of the KV cache (attn_decode_args.kv_dtype).
+ *   ATTN_KV_BF16      bf16 K and V, as in attn_decode.
+ *   ATTN_KV_FP8_E4M3  one byte per element, OCP 8-bit float E4M3 (1 sign bit, 4
+ *                     exponent bits with bias 7, 3 mantissa bits, exponent 0 =
+ *                     subnormals, S.1111.111 = NaN, no infinity); the attended key
+ *                     is k_scale * K and the value v_scale * V.  Halves the bytes a
+ *                     decode step streams (co-design page: TL;DR and checklist, FP8
+ *                     among the ways to shrink the KV state).  Every E4M3 value is
+ *                     a bf16 value, so the kernel widens K and V exactly and the
+ *                     rest of the computation is the bf16 path's.
+ */
+#define ATTN_KV_BF16 0
+#define ATTN_KV_FP8_E4M3 1
+
 /* Full-control decode.  Fields not listed keep the attn_decode meaning. */
 typedef struct attn_decode_args {
     const void *q;            /* bf16 [B][Hq][Hsz] */
-    const void *k_cache;      /* bf16 [B][KH][kv_stride][Hsz] */
-    const void *v_cache;      /* bf16 [B][KH][kv_stride][Hsz] */
+    const void *k_cache;      /* [B][KH][kv_stride][Hsz], element type kv_dtype */
+    const void *v_cache;      /* same layout and type as k_cache */
     const int32_t *seqlens;   /* HOST int32 [B], 0 <= L_b <= kv_stride */
     float *out;               /* fp32 [B][Hq][Hsz] */
     int B, Hq, KH, Hsz;
@@ -137,6 +152,9 @@ typedef struct attn_decode_args {
     int schedule;             /* ATTN_SCHEDULE_*; 0 = AUTO */
     int num_splits;           /* fixed split: chunks per (request, kv head); 0 = fill the GPU once.
                                  With more than one split, B*KH*num_splits <= ATTN_MAX_CTAS. */
+    int kv_dtype;             /* ATTN_KV_*; 0 = bf16 */
+    float k_scale;            /* FP8 only: key scale (<= 0 selects 1); must be 0 or 1 for bf16 */
+    float v_scale;            /* FP8 only: value scale (<= 0 selects 1); must be 0 or 1 for bf16 */
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);

@@ -107,6 +107,10 @@ def ex_args(**kw):
     (dict(num_splits=-2), A.ATTN_ERR_SHAPE),
     (dict(schedule=2, num_ctas=16), A.ATTN_ERR_SHAPE),       # the fixed split sets P itself
     (dict(schedule=2, num_splits=2000), A.ATTN_ERR_UNSUPPORTED),  # B*KH*splits > ATTN_MAX_CTAS
+    (dict(kv_dtype=2), A.ATTN_ERR_SHAPE),
+    (dict(kv_dtype=1, k_scale=float("inf")), A.ATTN_ERR_SHAPE),
+    (dict(kv_dtype=1, v_scale=float("nan")), A.ATTN_ERR_SHAPE),
+    (dict(kv_dtype=0, k_scale=0.5), A.ATTN_ERR_SHAPE),           # scales belong to FP8 caches
 ])
 def test_decode_ex_rejects_bad_arguments(kw, status):
     a, _sl = ex_args(**kw)
