@@ -51,6 +51,7 @@ class attn_decode_args(ctypes.Structure):
         ("ev_tiles_begin", _P), ("ev_tiles_end", _P),
         ("schedule", _I), ("num_splits", _I),
         ("kv_dtype", _I), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("block_table", _P), ("block_size", _I), ("max_blocks_per_seq", _I), ("num_blocks", _I),
     ]
 
 
@@ -206,7 +207,7 @@ class PreparedDecode:
     """
 
     def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
-                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0):
+                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, block_table=None):
         _bf16_cuda("q", q)
         kv_dtype = _kv_cuda("k_cache", k_cache)
         if _kv_cuda("v_cache", v_cache) != kv_dtype:
@@ -216,7 +217,9 @@ class PreparedDecode:
         self._sl = _host_seqlens(seqlens)
         if len(self._sl) != B:
             raise ValueError("seqlens must have B entries")
-        if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
+        if v_cache.shape != k_cache.shape or k_cache.shape[3] != Hsz:
+            raise ValueError("k_cache/v_cache must share one shape ending in Hsz")
+        if block_table is None and k_cache.shape[0] != B:
             raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
         if tuple(out.shape) != (B, Hq, Hsz) or not out.is_cuda or not out.is_contiguous():
             raise ValueError("out must be a contiguous fp32 CUDA tensor [B][Hq][Hsz]")
@@ -224,11 +227,15 @@ class PreparedDecode:
         a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
         a.seqlens, a.out = self._sl.ctypes.data, out.data_ptr()
         a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
-        a.kv_stride = S
+        a.kv_stride = 0 if block_table is not None else S
         a.scale = float(scale)
         a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
         a.schedule, a.num_splits = int(schedule), int(num_splits)
         a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
+        if block_table is not None:  # pools [num_blocks][KH][block_size][Hsz]
+            a.block_table = block_table.data_ptr()
+            a.block_size, a.max_blocks_per_seq, a.num_blocks = S, block_table.shape[1], k_cache.shape[0]
+            self._table = block_table
         self._args = a
         self._ref = ctypes.byref(a)
         self._fn = lib().attn_decode_ex
@@ -296,3 +303,42 @@ def attn_device_info():
 
 def attn_release():
     _check(lib().attn_release())
+
+
+def attn_decode_paged(q, k_pool, v_pool, block_table, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
+                      schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
+    """Decode over a paged KV cache (``attn_decode_ex`` with a block table).
+
+    k_pool, v_pool: [num_blocks][KH][block_size][Hsz] (bf16 or FP8 E4M3 codes);
+    block_table: int32 CUDA tensor [B][max_blocks_per_seq] of block ids.
+    """
+    import torch
+    _bf16_cuda("q", q)
+    kv_dtype = _kv_cuda("k_pool", k_pool)
+    if _kv_cuda("v_pool", v_pool) != kv_dtype or v_pool.shape != k_pool.shape:
+        raise TypeError("k_pool and v_pool must have the same shape and element type")
+    if block_table.dtype != torch.int32 or not block_table.is_cuda or not block_table.is_contiguous():
+        raise TypeError("block_table must be a contiguous int32 CUDA tensor")
+    B, Hq, Hsz = q.shape
+    nblocks, KH, bs, Hsz2 = k_pool.shape
+    if Hsz2 != Hsz or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("pools must be [num_blocks][KH][block_size][Hsz], block_table [B][max_blocks]")
+    sl = _host_seqlens(seqlens)
+    if len(sl) != B:
+        raise ValueError("seqlens must have B entries")
+    if out is None:
+        out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
+    a = attn_decode_args()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
+    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
+    a.kv_stride = 0
+    a.scale = float(scale)
+    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+    a.schedule, a.num_splits = int(schedule), int(num_splits)
+    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
+    a.block_table = block_table.data_ptr()
+    a.block_size, a.max_blocks_per_seq, a.num_blocks = bs, block_table.shape[1], nblocks
+    _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
+    return out
+

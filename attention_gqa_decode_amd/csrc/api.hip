@@ -215,9 +215,24 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (!(a->scale == a->scale) || isinf(a->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
     if (a->workspace && !aligned16(a->workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
 
+    int log2_bs = 0;
+    if (a->block_table) {
+        if (a->kv_stride != 0) return fail(ATTN_ERR_SHAPE, "kv_stride must be 0 with a block table");
+        if (a->block_size < 16 || (a->block_size & (a->block_size - 1)))
+            return fail(ATTN_ERR_UNSUPPORTED, "block_size=%d (supported: powers of two >= 16)", a->block_size);
+        if (a->max_blocks_per_seq <= 0 || a->num_blocks <= 0)
+            return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be positive");
+        if (((uintptr_t)a->block_table & 3u) != 0) return fail(ATTN_ERR_ALIGN, "block_table must be 4-byte aligned");
+        while ((1 << log2_bs) < a->block_size) ++log2_bs;
+    } else if (a->block_size != 0 || a->max_blocks_per_seq != 0 || a->num_blocks != 0) {
+        return fail(ATTN_ERR_SHAPE, "block_size, max_blocks_per_seq and num_blocks need a block table");
+    }
+
     const int G = a->Hq / a->KH;
     int64_t stride = a->kv_stride;
-    if (stride == 0) {
+    if (a->block_table) {
+        stride = (int64_t)a->max_blocks_per_seq * a->block_size;  // the longest context a table row can map
+    } else if (stride == 0) {
         for (int b = 0; b < a->B; ++b) stride = a->seqlens[b] > stride ? a->seqlens[b] : stride;
     }
     const int T = a->tile_keys > 0 ? a->tile_keys : attn::decode_tile_keys(a->Hsz);
@@ -239,6 +254,10 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     const float k_scale = fp8 && a->k_scale > 0.f ? a->k_scale : 1.f;
     p.scale_log2 = scale * k_scale * 1.4426950408889634f;
     p.v_scale = fp8 && a->v_scale > 0.f ? a->v_scale : 1.f;
+    p.block_table = a->block_table;
+    p.max_blocks_per_seq = a->max_blocks_per_seq;
+    p.log2_block_size = log2_bs;
+    p.num_blocks = a->num_blocks;
 
     int P = a->num_ctas;
     if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, G, a->Hsz) > a->workspace_bytes)

@@ -31,6 +31,10 @@ struct DecodeParams {
     int slot_floats;     // G*Hsz (O) + G (m) + G (l), rounded up to a multiple of 4
     float scale_log2;    // softmax scale * key scale * log2(e)
     float v_scale;       // value scale (1 for bf16 caches)
+    const int32_t *block_table;  // paged KV: [B][max_blocks_per_seq] block ids (NULL = contiguous)
+    int max_blocks_per_seq;
+    int log2_block_size;
+    int num_blocks;
     LeanPlan plan;
 };
 

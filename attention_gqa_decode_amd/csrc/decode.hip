@@ -93,9 +93,30 @@ struct Staged {
     u32x4 r[KvCfg<HSZ, FP8>::LOADS];
 };
 
-template <int HSZ, bool FP8>
-__device__ __forceinline__ void load_block(Staged<HSZ, FP8> &st, const uint8_t *kbase, const uint8_t *vbase, int key0,
-                                           int klast, int lane) {
+// Where the rows of one (request, kv head) context live.  Contiguous: row j of
+// the context is row j of [S][Hsz] at kbase/vbase.  Paged: row j sits in
+// physical block table[j >> log2_bs] of the pools [num_blocks][KH][bs][Hsz],
+// at in-block row j & (bs - 1); out-of-range block ids are clamped into the
+// pool, so a bad table gives wrong numbers, never an out-of-bounds access.
+template <bool PAGED>
+struct KvRows {
+    const uint8_t *kbase, *vbase;  // contiguous: this context; paged: the pools
+    const int32_t *table;          // paged: this request's row of the block table
+    int kh, KH, log2_bs, max_block;
+    __device__ __forceinline__ int64_t row_offset(int key, int row_bytes) const {
+        if constexpr (!PAGED) {
+            return (int64_t)key * row_bytes;
+        } else {
+            int blk = table[key >> log2_bs];
+            blk = blk < 0 ? 0 : (blk > max_block ? max_block : blk);
+            return ((((int64_t)blk * KH + kh) << log2_bs) + (key & ((1 << log2_bs) - 1))) * row_bytes;
+        }
+    }
+};
+
+template <int HSZ, bool FP8, bool PAGED>
+__device__ __forceinline__ void load_block(Staged<HSZ, FP8> &st, const KvRows<PAGED> &kv, int key0, int klast,
+                                           int lane) {
     using K = KvCfg<HSZ, FP8>;
     constexpr int HALF = K::LOADS / 2;
     constexpr int EB = FP8 ? 1 : 2;  // bytes per element
@@ -104,9 +125,9 @@ __device__ __forceinline__ void load_block(Staged<HSZ, FP8> &st, const uint8_t *
         const int c = 64 * j + lane;
         int key = key0 + c / K::CPR;
         key = key < klast ? key : klast;
-        const int64_t off = ((int64_t)key * HSZ + K::EPC * (c % K::CPR)) * EB;
-        st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off));
-        st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vbase + off));
+        const int64_t off = kv.row_offset(key, HSZ * EB) + K::EPC * (c % K::CPR) * EB;
+        st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kv.kbase + off));
+        st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kv.vbase + off));
     }
 }
 
@@ -378,7 +399,7 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
     }
 }
 
-template <int HSZ, bool FP8>
+template <int HSZ, bool FP8, bool PAGED>
 __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
     using C = DecodeCfg<HSZ>;
     constexpr int NS = C::NS;
@@ -436,9 +457,20 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     const int64_t t_end = plan_cta_begin(pl, c + 1);
     while (t < t_end) {
         const LeanPiece pc = plan_piece_at(pl, t, t_end);
-        const int64_t kvrow = ((int64_t)pc.b * pl.KH + pc.kh) * p.kv_stride;
-        const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k) + kvrow * HSZ * (FP8 ? 1 : 2);
-        const uint8_t *vbase = reinterpret_cast<const uint8_t *>(p.v) + kvrow * HSZ * (FP8 ? 1 : 2);
+        KvRows<PAGED> kv;
+        if constexpr (PAGED) {
+            kv.kbase = reinterpret_cast<const uint8_t *>(p.k);
+            kv.vbase = reinterpret_cast<const uint8_t *>(p.v);
+            kv.table = p.block_table + (int64_t)pc.b * p.max_blocks_per_seq;
+            kv.kh = pc.kh;
+            kv.KH = pl.KH;
+            kv.log2_bs = p.log2_block_size;
+            kv.max_block = p.num_blocks - 1;
+        } else {
+            const int64_t kvrow = ((int64_t)pc.b * pl.KH + pc.kh) * p.kv_stride;
+            kv.kbase = reinterpret_cast<const uint8_t *>(p.k) + kvrow * HSZ * (FP8 ? 1 : 2);
+            kv.vbase = reinterpret_cast<const uint8_t *>(p.v) + kvrow * HSZ * (FP8 ? 1 : 2);
+        }
         const int h0 = pc.kh * G;
 
         bf16x8 qop[NS];
@@ -465,7 +497,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         // of one wave executes in issue order, so no barrier is needed.
         Staged<HSZ, FP8> st;
         int blk = wave;
-        if (blk < nblk) load_block<HSZ, FP8>(st, kbase, vbase, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        if (blk < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + blk * kKeysPerBlock, klast, lane);
         while (blk < nblk) {
             store_block<HSZ, FP8>(st, stage, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -473,7 +505,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             int nxt = 0;
             if (lane == 0) nxt = atomicAdd(&blk_next, 1);
             nxt = __builtin_amdgcn_readfirstlane(nxt);
-            if (nxt < nblk) load_block<HSZ, FP8>(st, kbase, vbase, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
+            if (nxt < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
             process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, klast, col, grp, p.scale_log2,
                                m_run, l_run, oacc);
@@ -559,16 +591,24 @@ size_t tiles_lds_bytes(int Hsz, int G) {
     }
 }
 
-template <int HSZ, bool FP8>
+template <int HSZ, bool FP8, bool PAGED>
 hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
     const size_t lds = decode_tiles_lds_bytes<HSZ>(p.G);
     if (lds > 65536) {  // above the default dynamic-LDS limit; gfx950 has 160 KiB per CU
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8>), dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds, stream, p);
+    hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8, PAGED>), dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds,
+                       stream, p);
     return hipGetLastError();
+}
+
+template <int HSZ>
+hipError_t launch_tiles_h(const DecodeParams &p, bool fp8, hipStream_t stream) {
+    const bool paged = p.block_table != nullptr;
+    if (fp8) return paged ? launch_tiles_t<HSZ, true, true>(p, stream) : launch_tiles_t<HSZ, true, false>(p, stream);
+    return paged ? launch_tiles_t<HSZ, false, true>(p, stream) : launch_tiles_t<HSZ, false, false>(p, stream);
 }
 
 template <int HSZ>
@@ -576,9 +616,9 @@ int occupancy_t(int G) {
     int blocks = 0;
     const size_t lds = decode_tiles_lds_bytes<HSZ>(G);
     if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false>, DecodeCfg<HSZ>::W * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false, false>, DecodeCfg<HSZ>::W * 64,
                                                      decode_tiles_lds_bytes<HSZ>(G)) != hipSuccess)
         return 1;
     return blocks > 0 ? blocks : 1;
@@ -595,13 +635,10 @@ int decode_tile_keys(int Hsz) {
 }
 
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream) {
-    switch (Hsz * 2 + (fp8 ? 1 : 0)) {
-        case 128: return launch_tiles_t<64, false>(p, stream);
-        case 129: return launch_tiles_t<64, true>(p, stream);
-        case 256: return launch_tiles_t<128, false>(p, stream);
-        case 257: return launch_tiles_t<128, true>(p, stream);
-        case 512: return launch_tiles_t<256, false>(p, stream);
-        case 513: return launch_tiles_t<256, true>(p, stream);
+    switch (Hsz) {
+        case 64: return launch_tiles_h<64>(p, fp8, stream);
+        case 128: return launch_tiles_h<128>(p, fp8, stream);
+        case 256: return launch_tiles_h<256>(p, fp8, stream);
         default: return hipErrorInvalidValue;
     }
 }

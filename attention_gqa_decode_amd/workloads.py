@@ -164,3 +164,30 @@ def codes(t: torch.Tensor) -> np.ndarray:
     assert t.dtype == torch.uint8
     return t.detach().contiguous().cpu().numpy()
 
+
+def paged_layout(k: torch.Tensor, v: torch.Tensor, seqlens, block_size: int, seed: int, spare: int = 7):
+    """Scatter a contiguous [B][KH][S][Hsz] cache into block pools through a random block map.
+
+    Returns (k_pool, v_pool [num_blocks][KH][block_size][Hsz], block_table int32 [B][max_blocks]
+    on k's device).  Request b's logical block i lands in a random physical block; table
+    entries past a request's last block are -1 (never read); `spare` extra blocks stay zero.
+    """
+    B, KH, S, Hsz = k.shape
+    nb = [(int(L) + block_size - 1) // block_size for L in seqlens]
+    total = sum(nb) + spare
+    perm = np.random.default_rng(seed).permutation(total)
+    mb = max(max(nb), 1) + 2
+    table = np.full((B, mb), -1, dtype=np.int32)
+    kp = torch.zeros((total, KH, block_size, Hsz), dtype=k.dtype, device=k.device)
+    vp = torch.zeros_like(kp)
+    o = 0
+    for b in range(B):
+        for i in range(nb[b]):
+            blk = int(perm[o])
+            o += 1
+            table[b, i] = blk
+            n = min(block_size, int(seqlens[b]) - i * block_size)
+            kp[blk, :, :n] = k[b, :, i * block_size:i * block_size + n]
+            vp[blk, :, :n] = v[b, :, i * block_size:i * block_size + n]
+    return kp, vp, torch.from_numpy(table).to(k.device)
+

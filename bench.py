@@ -91,7 +91,7 @@ def log(msg: str) -> None:
 
 
 def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0,
-                 fp8: bool = False):
+                 fp8: bool = False, block_size: int = 0):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
     events recorded on the launch stream around every decode-kernel launch (roofline)."""
     import torch
@@ -111,7 +111,14 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     vs = [v] + [v.clone() for _ in range(copies - 1)]
     out = torch.empty((shape.B, shape.Hq, shape.Hsz), dtype=torch.float32, device="cuda")
     scale = shape.score_mult / math.sqrt(shape.Hsz) if shape.score_mult != 1.0 else 0.0
-    calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale, schedule=schedule) for i in range(copies)]
+    if block_size:  # paged pools, one block map per rotated copy
+        paged = [W.paged_layout(ks[i], vs[i], sl, block_size, seed=i) for i in range(copies)]
+        ks, vs = [p[0] for p in paged], [p[1] for p in paged]
+        calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale, schedule=schedule,
+                                  block_table=paged[i][2]) for i in range(copies)]
+        torch.cuda.empty_cache()
+    else:
+        calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale, schedule=schedule) for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         calls[i % copies](stream)
@@ -137,7 +144,8 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     nbytes = acc.decode_bytes(sl, shape.B, shape.Hq, shape.KH, shape.Hsz, kv_bytes=1 if fp8 else 2)
     kern_ms = sum(kern) / len(kern)
     res = {
-        "workload": shape.name + ("_fp8" if fp8 else ""), "kv_dtype": "fp8_e4m3" if fp8 else "bf16", "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
+        "workload": shape.name + ("_fp8" if fp8 else "") + (f"_paged{block_size}" if block_size else ""),
+        "kv_dtype": "fp8_e4m3" if fp8 else "bf16", "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
         "sum_kvsl": int(sum(sl)), "max_kvsl": int(max(sl)), "score_mult": shape.score_mult,
         "kv_copies_rotated": copies, "bytes_per_step": nbytes,
         "us_per_step": step_ms * 1e3, "GBps": nbytes / (step_ms * 1e-3) / 1e9,
@@ -281,6 +289,11 @@ def main():
         for name in ["llama3_8b", "long_mqa", "ragged"]:
             log(f"decode {name} with an FP8 E4M3 KV cache ...")
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev, fp8=True)
+            log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
+            others.append(o)
+        for bsz in (16, 64):
+            log(f"decode llama3_8b over a paged cache, block size {bsz} ...")
+            o = bench_decode(W.decode_workload("llama3_8b"), args.steps, args.warmup, hev, block_size=bsz)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
             others.append(o)
         log("schedules: stream-K vs fixed split ...")

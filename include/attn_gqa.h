@@ -155,6 +155,16 @@ typedef struct attn_decode_args {
     int kv_dtype;             /* ATTN_KV_*; 0 = bf16 */
     float k_scale;            /* FP8 only: key scale (<= 0 selects 1); must be 0 or 1 for bf16 */
     float v_scale;            /* FP8 only: value scale (<= 0 selects 1); must be 0 or 1 for bf16 */
+    /* Paged KV cache (block tables; "필수 LLM 최적화 기법(2)" section 3, PagedAttention).
+     * With a table, k_cache/v_cache are pools [num_blocks][KH][block_size][Hsz] and
+     * row j of request b lives in block block_table[b][j / block_size] at in-block row
+     * j % block_size; kv_stride must be 0 and every L_b <= max_blocks_per_seq *
+     * block_size.  Entries past a request's last block are never read; ids outside
+     * [0, num_blocks) are clamped into the pool (wrong numbers, never a bad access). */
+    const int32_t *block_table; /* DEVICE int32 [B][max_blocks_per_seq], or NULL = contiguous cache */
+    int block_size;           /* tokens per block: a power of two >= 16 */
+    int max_blocks_per_seq;   /* row stride of block_table */
+    int num_blocks;           /* blocks in each pool */
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);

@@ -111,6 +111,15 @@ def ex_args(**kw):
     (dict(kv_dtype=1, k_scale=float("inf")), A.ATTN_ERR_SHAPE),
     (dict(kv_dtype=1, v_scale=float("nan")), A.ATTN_ERR_SHAPE),
     (dict(kv_dtype=0, k_scale=0.5), A.ATTN_ERR_SHAPE),           # scales belong to FP8 caches
+    (dict(block_table=FAKE, block_size=24, max_blocks_per_seq=4, num_blocks=8), A.ATTN_ERR_UNSUPPORTED),
+    (dict(block_table=FAKE, block_size=8, max_blocks_per_seq=4, num_blocks=8), A.ATTN_ERR_UNSUPPORTED),
+    (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=0, num_blocks=8), A.ATTN_ERR_SHAPE),
+    (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=0), A.ATTN_ERR_SHAPE),
+    (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8, kv_stride=64), A.ATTN_ERR_SHAPE),
+    (dict(block_table=FAKE + 2, block_size=16, max_blocks_per_seq=4, num_blocks=8), A.ATTN_ERR_ALIGN),
+    (dict(block_size=16), A.ATTN_ERR_SHAPE),                      # block geometry without a table
+    (dict(seqlens=(4, 70), block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8),
+     A.ATTN_ERR_SHAPE),                                           # 70 keys > 4 blocks x 16
 ])
 def test_decode_ex_rejects_bad_arguments(kw, status):
     a, _sl = ex_args(**kw)
