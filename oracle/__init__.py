@@ -66,6 +66,9 @@ def _load():
     lib.oracle_decode_fp8_f64.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           _I64, ctypes.c_double, ctypes.c_double, ctypes.c_double, _P, _I64, _P]
     lib.oracle_decode_fp8_f64.restype = ctypes.c_int
+    lib.oracle_decode_multi_f64.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            _I64, ctypes.c_int, ctypes.c_double, _P, _I64, _P]
+    lib.oracle_decode_multi_f64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -202,5 +205,29 @@ def decode_fp8(q, k, v, seqlens, Hq: int, KH: int, scale: float, k_scale: float 
                                        float(k_scale), float(v_scale), rp, nr, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode_fp8_f64 rejected its arguments")
+    return out
+
+
+def decode_multi(q, k, v, seqlens, KH: int, scale: float, rows=None) -> np.ndarray:
+    """Multi-token decode: q uint16 [B][Hq][gamma][Hsz]; k, v uint16 [B][KH][S][Hsz].
+
+    Query t of request b attends keys 0 .. L_b - gamma + t.  Returns float64
+    [B][Hq][gamma][Hsz]; ``rows`` optionally lists flat ((b*Hq + h)*gamma + t) indices.
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, gamma, Hsz = q.shape
+    assert k.shape[0] == B and k.shape[1] == KH and k.shape[3] == Hsz and v.shape == k.shape
+    S = k.shape[2]
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    out = np.full(q.shape, np.nan)
+    if rows is None:
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rp, nr = _ptr(rows), rows.size
+    rc = _load().oracle_decode_multi_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), B, Hq, KH, Hsz, S, gamma,
+                                         float(scale), rp, nr, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode_multi_f64 rejected its arguments")
     return out
 

@@ -40,6 +40,13 @@
  *    infinity) with one scale per tensor: the attended key is k_scale * K and
  *    the value v_scale * V.  Decoded exactly to double.
  *
+ *  - Multi-token decode (lecture page, section 5 "추측 디코딩": the target model
+ *    checks the gamma drafted positions at once, like a short prefill, and
+ *    since decode is memory bound this costs little more than one token):
+ *    query t of gamma, at position L_b - gamma + t, attends to keys
+ *    0 .. L_b - gamma + t (the cache already holds the drafted tokens; a causal
+ *    mask aligned to the end of the context, which is the reading taken here).
+ *
  * Pins (tests/test_oracle.py): closed forms for one and two keys, q = 0 gives
  * the mean of V, constant V, V = identity gives the weights (rows sum to 1,
  * matched to scipy's softmax), key permutation and common key shift
@@ -272,6 +279,36 @@ int oracle_decode_fp8_f64(const uint16_t *q, const uint8_t *k, const uint8_t *v,
         }
         for (int d = 0; d < Hsz; ++d) dst[d] /= l;
         free(sc);
+    }
+    return 0;
+}
+
+/*
+ * Multi-token decode.  q, out [B][Hq][gamma][Hsz]; k, v [B][KH][S][Hsz] (bf16 bits).
+ * Row (b, h, t) attends keys 0 .. L_b - gamma + t of kv head h / G; a row whose
+ * range is empty (L_b - gamma + t < 0, e.g. L_b = 0) is zero.
+ * rows: optional list of flat ((b*Hq + h)*gamma + t) indices (NULL = all).
+ */
+int oracle_decode_multi_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const int32_t *seqlens, int B, int Hq, int KH, int Hsz, int64_t S,
+                            int gamma, double scale, const int64_t *rows, int64_t nrows, double *out) {
+    if (!q || !k || !v || !seqlens || !out || !dims_ok(B, Hq, KH, Hsz) || S < 0 || gamma < 1) return -1;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] > S) return -1;
+    int G = Hq / KH;
+    int64_t total = rows ? nrows : (int64_t)B * Hq * gamma;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < total; ++r) {
+        int64_t idx = rows ? rows[r] : r;
+        int64_t bh = idx / gamma;
+        int t = (int)(idx % gamma);
+        int b = (int)(bh / Hq), h = (int)(bh % Hq);
+        int kh = h / G;
+        int64_t last = (int64_t)seqlens[b] - gamma + t;  /* last visible key */
+        const uint16_t *kb = k + ((int64_t)b * KH + kh) * S * Hsz;
+        const uint16_t *vb = v + ((int64_t)b * KH + kh) * S * Hsz;
+        attend_rows(q + idx * Hsz, kb, vb, 0, last + 1 > 0 ? last + 1 : 0, Hsz, scale, 1, out + idx * Hsz,
+                    NULL, NULL);
     }
     return 0;
 }

@@ -403,3 +403,57 @@ def test_fp8_decode_closed_forms(oracle):
     vc = np.full((1, 1, 5, Hsz), 0x3C, dtype=np.uint8)  # 1.5
     out = oracle.decode_fp8(q, k8, vc, [5], 4, 1, 0.125, 3.0, 2.0)
     np.testing.assert_allclose(out, 3.0, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------- multi-token decode
+
+def test_multi_gamma1_is_decode(oracle):
+    rng = np.random.default_rng(70)
+    B, Hq, KH, Hsz, S = 3, 8, 2, 64, 40
+    sl = [40, 0, 17]
+    q, k, v = rand_bits(rng, (B, Hq, 1, Hsz)), rand_bits(rng, (B, KH, S, Hsz)), rand_bits(rng, (B, KH, S, Hsz))
+    a = oracle.decode_multi(q, k, v, sl, KH, 0.125)[:, :, 0]
+    b = oracle.decode(np.ascontiguousarray(q[:, :, 0]), k, v, sl, Hq, KH, 0.125)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("gamma", [2, 4, 7])
+def test_multi_equals_last_rows_of_causal_prefill(oracle, gamma):
+    # gamma drafted positions checked at once are the last gamma rows of a causal prefill
+    # over the whole context (the lecture: the target model scores them "like prefill")
+    rng = np.random.default_rng(71 + gamma)
+    Hq, KH, Hsz, L = 8, 2, 64, 29
+    qf = rand_bits(rng, (1, Hq, L, Hsz))
+    k, v = rand_bits(rng, (1, KH, L, Hsz)), rand_bits(rng, (1, KH, L, Hsz))
+    pre = oracle.prefill_causal(qf, k, v, KH, 0.125)
+    got = oracle.decode_multi(np.ascontiguousarray(qf[:, :, L - gamma:]), k, v, [L], KH, 0.125)
+    np.testing.assert_allclose(got, pre[:, :, L - gamma:], rtol=1e-13, atol=1e-15)
+
+
+def test_multi_matches_torch_sdpa_with_end_aligned_mask(oracle):
+    rng = np.random.default_rng(73)
+    B, Hq, KH, Hsz, S, gamma = 2, 8, 4, 64, 50, 5
+    sl = [50, 23]
+    q, k, v = rand_bits(rng, (B, Hq, gamma, Hsz)), rand_bits(rng, (B, KH, S, Hsz)), rand_bits(rng, (B, KH, S, Hsz))
+    out = oracle.decode_multi(q, k, v, sl, KH, 0.125)
+    qt, kt, vt = (torch.from_numpy(bits_to_f64(x)) for x in (q, k, v))
+    for b, L in enumerate(sl):
+        mask = torch.arange(L)[None, :] <= (L - gamma + torch.arange(gamma))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[b][None], kt[b, :, :L].repeat_interleave(Hq // KH, 0)[None],
+            vt[b, :, :L].repeat_interleave(Hq // KH, 0)[None], attn_mask=mask, scale=0.125)
+        np.testing.assert_allclose(out[b], ref[0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_multi_first_draft_sees_the_prefix_only(oracle):
+    # with V = e_j, the output of draft t is its weight vector: zero on keys after L - gamma + t
+    rng = np.random.default_rng(74)
+    Hsz, L, gamma = 64, 20, 4
+    q = rand_bits(rng, (1, 1, gamma, Hsz), 2.0)
+    k = rand_bits(rng, (1, 1, L, Hsz))
+    v = bf16_bits(np.eye(L, Hsz)[None, None])
+    out = oracle.decode_multi(q, k, v, [L], 1, 0.125)[0, 0]
+    for t in range(gamma):
+        last = L - gamma + t
+        assert np.all(out[t, last + 1:] == 0) and out[t, last] > 0
+        assert abs(out[t].sum() - 1.0) < 1e-12

@@ -34,6 +34,8 @@ MUTANTS = {
     "fp8_v_scale_dropped": ("dst[d] += w * (v_scale * oracle_fp8_e4m3_to_f64(vb[j * Hsz + d]));",
                             "dst[d] += w * oracle_fp8_e4m3_to_f64(vb[j * Hsz + d]);"),
     "fp8_k_scale_dropped": ("(k_scale * oracle_fp8_e4m3_to_f64(kb[j * Hsz + d]))", "oracle_fp8_e4m3_to_f64(kb[j * Hsz + d])"),
+    "multi_mask_off_by_one": ("int64_t last = (int64_t)seqlens[b] - gamma + t;", "int64_t last = (int64_t)seqlens[b] - gamma + t - 1;"),
+    "multi_mask_top_left": ("int64_t last = (int64_t)seqlens[b] - gamma + t;", "int64_t last = t;"),
     "prefill_wrong_kv_head": ("const uint16_t *kb = k + ((int64_t)b * KH + kh) * ISL * Hsz;",
                               "const uint16_t *kb = k + ((int64_t)b * KH + (h % KH)) * ISL * Hsz;"),
 }
@@ -55,6 +57,9 @@ PIN_CALLS = [
     (pins.test_fp8_e4m3_all_codes_match_torch, {}),
     (pins.test_fp8_decode_equals_bf16_decode_of_the_same_values, {"k_scale": 0.5, "v_scale": 4.0}),
     (pins.test_fp8_decode_closed_forms, {}),
+    (pins.test_multi_gamma1_is_decode, {}),
+    (pins.test_multi_equals_last_rows_of_causal_prefill, {"gamma": 4}),
+    (pins.test_multi_first_draft_sees_the_prefix_only, {}),
 ]
 
 
