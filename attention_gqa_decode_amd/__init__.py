@@ -52,6 +52,7 @@ class attn_decode_args(ctypes.Structure):
         ("schedule", _I), ("num_splits", _I),
         ("kv_dtype", _I), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("block_table", _P), ("block_size", _I), ("max_blocks_per_seq", _I), ("num_blocks", _I),
+        ("q_len", _I),
     ]
 
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_ex.restype = _I
     L.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_decode_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.attn_decode_multi_workspace_bytes.restype = ctypes.c_size_t
     L.attn_prefill_causal.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]
     L.attn_prefill_causal.restype = _I
     L.attn_decode_plan.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P]
@@ -339,6 +342,43 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seqlens, out=None, *, scal
     a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
     a.block_table = block_table.data_ptr()
     a.block_size, a.max_blocks_per_seq, a.num_blocks = bs, block_table.shape[1], nblocks
+    _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
+    return out
+
+
+def attn_decode_multi_workspace_bytes(B: int, Hq: int, KH: int, Hsz: int, q_len: int, num_ctas: int = 0) -> int:
+    return int(lib().attn_decode_multi_workspace_bytes(B, Hq, KH, Hsz, q_len, num_ctas))
+
+
+def attn_decode_multi(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
+                      schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
+    """Multi-token decode (``attn_decode_ex`` with q_len = gamma): q [B][Hq][gamma][Hsz] bf16,
+    caches [B][KH][S][Hsz] holding the drafted tokens last; query t attends keys
+    0 .. L_b - gamma + t.  Returns out fp32 [B][Hq][gamma][Hsz]."""
+    import torch
+    _bf16_cuda("q", q)
+    kv_dtype = _kv_cuda("k_cache", k_cache)
+    if _kv_cuda("v_cache", v_cache) != kv_dtype:
+        raise TypeError("k_cache and v_cache must have the same element type")
+    B, Hq, gamma, Hsz = q.shape
+    KH, S = k_cache.shape[1], k_cache.shape[2]
+    sl = _host_seqlens(seqlens)
+    if len(sl) != B:
+        raise ValueError("seqlens must have B entries")
+    if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
+    if out is None:
+        out = torch.empty((B, Hq, gamma, Hsz), dtype=torch.float32, device=q.device)
+    a = attn_decode_args()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
+    a.kv_stride = S
+    a.scale = float(scale)
+    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+    a.schedule, a.num_splits = int(schedule), int(num_splits)
+    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
+    a.q_len = gamma
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
     return out
 

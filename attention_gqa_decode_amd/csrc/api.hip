@@ -176,13 +176,18 @@ const char *attn_status_string(int status) {
 
 const char *attn_last_error(void) { return g_last_error.c_str(); }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas) {
-    if (check_decode_dims(B, Hq, KH, Hsz) != ATTN_OK || num_ctas < 0) return 0;
-    const int G = Hq / KH;
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int KH, int Hsz, int q_len, int num_ctas) {
+    if (check_decode_dims(B, Hq, KH, Hsz) != ATTN_OK || num_ctas < 0 || q_len < 0) return 0;
+    const int NC = (Hq / KH) * (q_len > 1 ? q_len : 1);
+    if (NC > attn::kMaxGroup) return 0;
     int P = num_ctas;
-    if (P == 0 && device_default_ctas(Hsz, G, &P) != ATTN_OK) return 0;
+    if (P == 0 && device_default_ctas(Hsz, NC, &P) != ATTN_OK) return 0;
     if (P > attn::kMaxCtas) return 0;
-    return attn::decode_workspace_bytes(P, G, Hsz);
+    return attn::decode_workspace_bytes(P, NC, Hsz);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas) {
+    return attn_decode_multi_workspace_bytes(B, Hq, KH, Hsz, 1, num_ctas);
 }
 
 int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
@@ -197,6 +202,13 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (a->kv_stride < 0) return fail(ATTN_ERR_SHAPE, "kv_stride=%lld is negative", (long long)a->kv_stride);
     if (a->tile_keys < 0 || a->num_ctas < 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be >= 0");
     if (a->num_ctas > attn::kMaxCtas) return fail(ATTN_ERR_UNSUPPORTED, "num_ctas=%d exceeds %d", a->num_ctas, attn::kMaxCtas);
+    if (a->q_len < 0) return fail(ATTN_ERR_SHAPE, "q_len=%d is negative", a->q_len);
+    const int qlen = a->q_len > 1 ? a->q_len : 1;
+    if ((a->Hq / a->KH) * qlen > attn::kMaxGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "G*q_len=%d exceeds %d query columns", (a->Hq / a->KH) * qlen, attn::kMaxGroup);
+    for (int b = 0; b < a->B; ++b)
+        if (a->seqlens[b] != 0 && a->seqlens[b] < qlen)
+            return fail(ATTN_ERR_SHAPE, "seqlens[%d]=%d holds fewer keys than q_len=%d", b, a->seqlens[b], qlen);
     if (a->schedule < ATTN_SCHEDULE_AUTO || a->schedule > ATTN_SCHEDULE_FIXED_SPLIT)
         return fail(ATTN_ERR_SHAPE, "schedule=%d is not an ATTN_SCHEDULE_* value", a->schedule);
     if (a->num_splits < 0) return fail(ATTN_ERR_SHAPE, "num_splits=%d is negative", a->num_splits);
@@ -248,7 +260,9 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.kv_stride = stride;
     p.Hq = a->Hq;
     p.G = G;
-    p.slot_floats = attn::decode_slot_floats(G, a->Hsz);
+    p.qlen = qlen;
+    p.NC = G * qlen;
+    p.slot_floats = attn::decode_slot_floats(p.NC, a->Hsz);
     const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Hsz);
     const bool fp8 = a->kv_dtype == ATTN_KV_FP8_E4M3;
     const float k_scale = fp8 && a->k_scale > 0.f ? a->k_scale : 1.f;
@@ -260,13 +274,13 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.num_blocks = a->num_blocks;
 
     int P = a->num_ctas;
-    if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, G, a->Hsz) > a->workspace_bytes)
+    if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, p.NC, a->Hsz) > a->workspace_bytes)
         return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for num_ctas=%d", a->workspace_bytes,
-                    attn::decode_workspace_bytes(P, G, a->Hsz), P);
+                    attn::decode_workspace_bytes(P, p.NC, a->Hsz), P);
 
     // ---- argument checks done; HIP calls from here on ----
     int resident = 0;
-    st = device_default_ctas(a->Hsz, G, &resident);
+    st = device_default_ctas(a->Hsz, p.NC, &resident);
     if (st != ATTN_OK) return st;
     // The selector (the digest's runtime selection policy: stream-K tiles for
     // long, few-head or ragged work; no split when the batch alone fills every
@@ -291,7 +305,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.counters = nullptr;
 
     if (p.plan.N > 0 && any_split_segment(p.plan)) {
-        const size_t need = attn::decode_workspace_bytes(P, G, a->Hsz);
+        const size_t need = attn::decode_workspace_bytes(P, p.NC, a->Hsz);
         char *w = nullptr;
         if (a->workspace) {
             if (a->workspace_bytes < need)

@@ -28,7 +28,9 @@ struct DecodeParams {
     int64_t kv_stride;   // S
     int Hq;
     int G;
-    int slot_floats;     // G*Hsz (O) + G (m) + G (l), rounded up to a multiple of 4
+    int qlen;            // query tokens per request (1 = plain decode; gamma for drafted tokens)
+    int NC;              // MFMA columns in use: G * qlen <= 16, column c = (token c / G, head c % G)
+    int slot_floats;     // NC*Hsz (O) + NC (m) + NC (l), rounded up to a multiple of 4
     float scale_log2;    // softmax scale * key scale * log2(e)
     float v_scale;       // value scale (1 for bf16 caches)
     const int32_t *block_table;  // paged KV: [B][max_blocks_per_seq] block ids (NULL = contiguous)
@@ -38,8 +40,8 @@ struct DecodeParams {
     LeanPlan plan;
 };
 
-// Partial slot layout: O[G][Hsz] unnormalised, then m[G] (log2 domain), then l[G].
-inline int decode_slot_floats(int G, int Hsz) { return (G * Hsz + 2 * G + 3) & ~3; }
+// Partial slot layout: O[NC][Hsz] unnormalised, then m[NC] (log2 domain), then l[NC].
+inline int decode_slot_floats(int NC, int Hsz) { return (NC * Hsz + 2 * NC + 3) & ~3; }
 
 // Split heads are merged inside the tile kernel by a tree of fan-in kMergeFanIn:
 // the last CTA to arrive at a group merges it.  kMergeLevels levels cover
@@ -51,14 +53,14 @@ constexpr int kMaxCtas = 4096;
 // Workspace layout: int counters[kMergeLevels][2 * kMaxCtas] (a fixed-size
 // region, so its place never depends on P), then float slots[2P][slot_floats].
 constexpr size_t kCounterBytes = (size_t)kMergeLevels * 2 * kMaxCtas * sizeof(int);
-inline size_t decode_workspace_bytes(int P, int G, int Hsz) {
-    return kCounterBytes + (size_t)2 * P * decode_slot_floats(G, Hsz) * sizeof(float);
+inline size_t decode_workspace_bytes(int P, int NC, int Hsz) {
+    return kCounterBytes + (size_t)2 * P * decode_slot_floats(NC, Hsz) * sizeof(float);
 }
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
-int decode_tiles_occupancy(int Hsz, int G);  // resident decode workgroups per CU
+int decode_tiles_occupancy(int Hsz, int NC);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                                  int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,

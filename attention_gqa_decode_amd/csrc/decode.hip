@@ -178,10 +178,12 @@ __device__ __forceinline__ void store_block(const Staged<HSZ, FP8> &st, uint16_t
 
 __device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-// BMM1 -> online softmax -> BMM2 for one staged 32-key block of one wave.
+// BMM1 -> online softmax -> BMM2 for one staged 32-key block of one wave; keys
+// after kmax (the piece's end, or the causal limit of the lane's drafted token)
+// are masked.
 template <int HSZ>
 __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[HSZ / 32],
-                                              const bf16x8 (&sel)[2], int key0, int klast, int col, int grp,
+                                              const bf16x8 (&sel)[2], int key0, int kmax, int col, int grp,
                                               float scale_log2, float &m_run, float &l_run,
                                               f32x4 (&oacc)[HSZ / 16]) {
     using C = DecodeCfg<HSZ>;
@@ -205,18 +207,20 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = key0 + 16 * kb + 4 * grp + i;
-            const float xv = key <= klast ? sc[kb][i] * scale_log2 : NEG_INF;
+            const float xv = key <= kmax ? sc[kb][i] * scale_log2 : NEG_INF;
             x[4 * kb + i] = xv;
             mx = fmaxf(mx, xv);
         }
     mx = wave_max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);  // finite: every processed block holds a valid key
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, mx);
+    // -inf only while a drafted token's column has seen no key yet (its limit lies before this block)
+    const float m_use = m_new == NEG_INF ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ps = 0.f;
     bf16x8 phi, plo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(x[i] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(x[i] - m_use);
         ps += pv;
         const __bf16 hi = (__bf16)pv;
         phi[i] = hi;
@@ -301,14 +305,14 @@ __device__ __forceinline__ int partial_slot(const LeanPlan &pl, int c_lo, int64_
 // All control flow is uniform over the CTA.
 template <int HSZ, int NT>
 __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPiece &pc, int c, int *flag) {
-    const int G = p.G;
+    const int NC = p.NC, G = p.G;
     const int tid = threadIdx.x;
     const int nb = (int)(pc.seg_end - pc.seg_begin);
     const int c_lo = plan_cta_of_tile(pl, pc.seg_begin);
     const int k = plan_cta_of_tile(pl, pc.seg_begin + nb - 1) - c_lo + 1;  // partials of this head
     int i = c - c_lo;  // index of the state this CTA carries up the tree
     int span = 1;      // partials covered by one state at the current level
-    constexpr int UNITS = kMaxGroup * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound
+    constexpr int UNITS = kMaxGroup * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound (NC <= 16)
     for (int level = 0; level < kMergeLevels; ++level) {
         const MergeGroup mg = plan_merge_group(k, i, span, kMergeFanIn);
         const int first = mg.first, n = mg.n;
@@ -329,7 +333,7 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
             continue;
         }
         // merge states first .. first+n-1 of this level
-        const int units = G * HSZ / 4;
+        const int units = NC * HSZ / 4;
         f32x4 res[UNITS];
         float Lsum[UNITS], Mmax[UNITS];
 #pragma unroll
@@ -349,19 +353,21 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
                 ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (j < n) {
                     const float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, (first + j) * span) * p.slot_floats;
-                    mv[j] = ld_shared_f(sp + G * HSZ + g);
-                    lv[j] = ld_shared_f(sp + G * HSZ + G + g);
+                    mv[j] = ld_shared_f(sp + NC * HSZ + g);
+                    lv[j] = ld_shared_f(sp + NC * HSZ + NC + g);
                     ov[j] = ld_shared_f4(sp + g * HSZ + 4 * d4);
                 }
             }
             float M = mv[0];
 #pragma unroll
             for (int j = 1; j < kMergeFanIn; ++j) M = fmaxf(M, mv[j]);
+            // M is -inf only for a drafted token whose limit lies before every member's keys
+            const float Muse = M == -__builtin_inff() ? 0.f : M;
             float L = 0.f;
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < kMergeFanIn; ++j) {
-                const float f = j < n ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;  // every state is non-empty
+                const float f = j < n ? __builtin_amdgcn_exp2f(mv[j] - Muse) : 0.f;
                 L += lv[j] * f;
                 O += ov[j] * f;
             }
@@ -374,8 +380,8 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
             for (int r = 0; r < UNITS; ++r) {
                 const int u = tid + r * NT;
                 if (u >= units) continue;
-                const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
-                float *dst = p.out + ((int64_t)pc.b * p.Hq + pc.kh * G + g) * HSZ + 4 * d4;
+                const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);  // column g: token g / G, head g % G
+                float *dst = p.out + (((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
                 *reinterpret_cast<f32x4 *>(dst) = res[r] * (p.v_scale / Lsum[r]);
             }
             return;
@@ -389,8 +395,8 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
             const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
             st_shared_f4(sp + g * HSZ + 4 * d4, res[r]);
             if (d4 == 0) {
-                st_shared_f(sp + G * HSZ + g, Mmax[r]);
-                st_shared_f(sp + G * HSZ + G + g, Lsum[r]);
+                st_shared_f(sp + NC * HSZ + g, Mmax[r]);
+                st_shared_f(sp + NC * HSZ + NC + g, Lsum[r]);
             }
         }
         wait_memory();
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     const int col = lane & 15;  // head g (Q, P, O), key row (K, V) or d (V^T)
     const int grp = lane >> 4;  // 8-wide slice of the MFMA contraction
     const int c = blockIdx.x;
-    const int G = p.G;
+    const int G = p.G, NC = p.NC;
     const float NEG_INF = -__builtin_inff();
     uint16_t *stage = stages + wave * C::STAGE;
 
@@ -448,8 +454,8 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     // Requests with an empty context own no tiles: their output rows are zero.
     for (int b = c; b < pl.B; b += pl.P) {
         if (pl.seqlen[b] != 0) continue;
-        float *orow = p.out + (int64_t)b * p.Hq * HSZ;
-        for (int e = threadIdx.x; e < p.Hq * HSZ / 4; e += W * 64)
+        float *orow = p.out + (int64_t)b * p.Hq * p.qlen * HSZ;
+        for (int e = threadIdx.x; e < p.Hq * p.qlen * HSZ / 4; e += W * 64)
             reinterpret_cast<f32x4 *>(orow)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
@@ -474,11 +480,13 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         const int h0 = pc.kh * G;
 
         bf16x8 qop[NS];
-        const uint16_t *qrow = p.q + ((int64_t)pc.b * p.Hq + h0 + (col < G ? col : 0)) * HSZ;
+        // column col holds query token col / G of head h0 + col % G (q is [B][Hq][qlen][Hsz])
+        const int ccol = col < NC ? col : 0;
+        const uint16_t *qrow = p.q + (((int64_t)pc.b * p.Hq + h0 + ccol % G) * p.qlen + ccol / G) * HSZ;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             bf16x8 z = {};
-            qop[s] = col < G ? load_row8(qrow + 32 * s + 8 * grp) : z;
+            qop[s] = col < NC ? load_row8(qrow + 32 * s + 8 * grp) : z;
         }
 
         float m_run = NEG_INF;  // running max (log2 domain) of head `col`
@@ -489,6 +497,9 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
 
         const int nblk = (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
         const int klast = pc.key_end - 1;
+        // drafted token t (column col) sees keys up to L_b - qlen + t
+        const int climit = pl.seqlen[pc.b] - p.qlen + ccol / G;
+        const int kmax = klast < climit ? klast : climit;
         // Block w starts on wave w; every wave claims its next block from an
         // LDS counter when it starts computing one, so waves whose loads come
         // back sooner take more blocks and all waves of the CTA finish within
@@ -507,7 +518,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, klast, col, grp, p.scale_log2,
+            process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, kmax, col, grp, p.scale_log2,
                                m_run, l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -537,14 +548,14 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         for (int db = 0; db < ND; ++db) oacc[db] *= f;
 #pragma unroll
         for (int half = W / 2; half >= 1; half >>= 1) {
-            if (wave >= half && wave < 2 * half && col < G) {
-                float *dst = sm_o + ((wave - half) * G + col) * OSTRIDE + 4 * grp;
+            if (wave >= half && wave < 2 * half && col < NC) {
+                float *dst = sm_o + ((wave - half) * NC + col) * OSTRIDE + 4 * grp;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db];
             }
             __syncthreads();
-            if (wave < half && col < G) {
-                const float *src = sm_o + (wave * G + col) * OSTRIDE + 4 * grp;
+            if (wave < half && col < NC) {
+                const float *src = sm_o + (wave * NC + col) * OSTRIDE + 4 * grp;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) oacc[db] += *reinterpret_cast<const f32x4 *>(src + 16 * db);
             }
@@ -552,10 +563,10 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         }
 
         const bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
-        if (wave == 0 && col < G) {
+        if (wave == 0 && col < NC) {
             if (whole) {
                 const float inv = p.v_scale / Lt;
-                float *dst = p.out + ((int64_t)pc.b * p.Hq + h0 + col) * HSZ + 4 * grp;
+                float *dst = p.out + (((int64_t)pc.b * p.Hq + h0 + col % G) * p.qlen + col / G) * HSZ + 4 * grp;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db] * inv;
             } else {
@@ -564,8 +575,8 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
 #pragma unroll
                 for (int db = 0; db < ND; ++db) st_shared_f4(dst + 16 * db, oacc[db]);
                 if (grp == 0) {
-                    st_shared_f(slot + G * HSZ + col, M);
-                    st_shared_f(slot + G * HSZ + G + col, Lt);
+                    st_shared_f(slot + NC * HSZ + col, M);
+                    st_shared_f(slot + NC * HSZ + NC + col, Lt);
                 }
             }
             if (!whole) wait_memory();
@@ -593,7 +604,7 @@ size_t tiles_lds_bytes(int Hsz, int G) {
 
 template <int HSZ, bool FP8, bool PAGED>
 hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
-    const size_t lds = decode_tiles_lds_bytes<HSZ>(p.G);
+    const size_t lds = decode_tiles_lds_bytes<HSZ>(p.NC);
     if (lds > 65536) {  // above the default dynamic-LDS limit; gfx950 has 160 KiB per CU
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -157,6 +157,39 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     return res
 
 
+def bench_multi(shape, gamma: int, steps: int, warmup: int):
+    """Multi-token decode (gamma drafted tokens per request, one pass over K/V)."""
+    import torch
+
+    import attention_gqa_decode_amd as A
+    from attention_gqa_decode_amd import accounting as acc
+    from attention_gqa_decode_amd import workloads as W
+
+    q = W.randn_bf16((shape.B, shape.Hq, gamma, shape.Hsz), shape.seed, "cuda")
+    _, k, v, sl = W.decode_inputs(shape, device="cuda")
+    sl = sl.tolist()
+    kv_read = 2 * shape.KH * sum(sl) * shape.Hsz * 2
+    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(kv_read, 1))))
+    ks = [k] + [k.clone() for _ in range(copies - 1)]
+    vs = [v] + [v.clone() for _ in range(copies - 1)]
+    out = torch.empty((shape.B, shape.Hq, gamma, shape.Hsz), dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        A.attn_decode_multi(q, ks[i % copies], vs[i % copies], sl, out=out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        A.attn_decode_multi(q, ks[i % copies], vs[i % copies], sl, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    nbytes = kv_read + shape.B * shape.Hq * gamma * shape.Hsz * (2 + 4)
+    del q, ks, vs, out
+    torch.cuda.empty_cache()
+    return {"workload": f"{shape.name}_multi{gamma}", "q_len": gamma, "us_per_step": ms * 1e3,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes_per_step": nbytes}
+
+
 def bench_prefill(steps: int, warmup: int):
     import torch
 
@@ -278,6 +311,7 @@ def main():
     log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, kernel {r['kernel_us']:.1f} us")
     others = []
     schedules = []
+    multi = None
     probe = None
     prefill = None
     if not args.headline_only:
@@ -296,6 +330,9 @@ def main():
             o = bench_decode(W.decode_workload("llama3_8b"), args.steps, args.warmup, hev, block_size=bsz)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
             others.append(o)
+        log("multi-token decode (4 drafted tokens) on llama3_8b ...")
+        multi = bench_multi(W.decode_workload("llama3_8b"), 4, args.steps, args.warmup)
+        log(f"  {multi['us_per_step']:.1f} us/step for 4 tokens")
         log("schedules: stream-K vs fixed split ...")
         for name in ["llama3_8b", "long_mqa", "ragged"]:
             shp = W.decode_workload(name)
@@ -343,6 +380,7 @@ def main():
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],
         "schedules": schedules,
+        "multi_token": multi,
         "prefill": prefill,
         "hbm_probes": probe,
     }

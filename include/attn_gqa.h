@@ -165,6 +165,12 @@ typedef struct attn_decode_args {
     int block_size;           /* tokens per block: a power of two >= 16 */
     int max_blocks_per_seq;   /* row stride of block_table */
     int num_blocks;           /* blocks in each pool */
+    /* Multi-token decode (speculative verification; lecture page "추론 최적화", section 5:
+     * the target model checks gamma drafted tokens at once).  With q_len = gamma > 1, q
+     * and out are [B][Hq][gamma][Hsz], the cache already holds the drafted tokens as
+     * the last gamma of each context, and query t attends keys 0 .. L_b - gamma + t.
+     * Needs G * gamma <= ATTN_MAX_GROUP and L_b = 0 or L_b >= gamma. */
+    int q_len;                /* 0 or 1 = one query token per request */
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
@@ -177,6 +183,10 @@ int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
  * up to 16 bytes.  Returns 0 for unsupported sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas);
+
+/* The same for multi-token decode with q_len query tokens per request (slots hold
+ * G * q_len states); q_len <= 1 gives attn_decode_workspace_bytes. */
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int KH, int Hsz, int q_len, int num_ctas);
 
 /*
  * attn_prefill_causal -- causal GQA attention over a whole prompt.

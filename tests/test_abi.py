@@ -118,6 +118,9 @@ def ex_args(**kw):
     (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8, kv_stride=64), A.ATTN_ERR_SHAPE),
     (dict(block_table=FAKE + 2, block_size=16, max_blocks_per_seq=4, num_blocks=8), A.ATTN_ERR_ALIGN),
     (dict(block_size=16), A.ATTN_ERR_SHAPE),                      # block geometry without a table
+    (dict(q_len=-1), A.ATTN_ERR_SHAPE),
+    (dict(q_len=5), A.ATTN_ERR_UNSUPPORTED),                      # G * q_len = 20 > 16 query columns
+    (dict(Hq=2, KH=2, q_len=5), A.ATTN_ERR_SHAPE),                 # 4 cached keys < 5 query tokens
     (dict(seqlens=(4, 70), block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8),
      A.ATTN_ERR_SHAPE),                                           # 70 keys > 4 blocks x 16
 ])
@@ -167,6 +170,9 @@ def test_workspace_bytes_formula():
     assert A.attn_decode_workspace_bytes(1, 8, 1, 64, 7) == C + 2 * 7 * ((8 * 64 + 16 + 3) & ~3) * 4
     assert A.attn_decode_workspace_bytes(1, 8, 3, 64, 7) == 0  # Hq % KH != 0
     assert A.attn_decode_workspace_bytes(1, 8, 1, 64, A.ATTN_MAX_CTAS + 1) == 0
+    # multi-token: slots hold G * q_len states
+    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 4, 100) == C + 2 * 100 * ((16 * 128 + 32 + 3) & ~3) * 4
+    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 5, 100) == 0  # 20 columns
 
 
 def test_python_binding_validates_cache_capacity():
