@@ -353,6 +353,7 @@ int attn_decode_plan(const int32_t *seqlens, int B, int KH, int tile_keys, int n
     if (B <= 0 || KH <= 0) return fail(ATTN_ERR_SHAPE, "B and KH must be positive");
     if (B > ATTN_MAX_BATCH) return fail(ATTN_ERR_UNSUPPORTED, "B=%d exceeds %d", B, ATTN_MAX_BATCH);
     if (tile_keys <= 0 || num_ctas <= 0) return fail(ATTN_ERR_SHAPE, "tile_keys and num_ctas must be positive");
+    if (num_ctas > attn::kMaxCtas) return fail(ATTN_ERR_UNSUPPORTED, "num_ctas=%d exceeds %d", num_ctas, attn::kMaxCtas);
     LeanPlan plan;
     int st = build_plan(seqlens, B, KH, tile_keys, -1, &plan);
     if (st != ATTN_OK) return st;

@@ -405,6 +405,54 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
     }
 }
 
+// K/V rows of the context of request b under kv head kh.
+template <int HSZ, bool FP8, bool PAGED>
+__device__ __forceinline__ KvRows<PAGED> piece_rows(const DecodeParams &p, const LeanPlan &pl, int b, int kh) {
+    KvRows<PAGED> kv;
+    if constexpr (PAGED) {
+        kv.kbase = reinterpret_cast<const uint8_t *>(p.k);
+        kv.vbase = reinterpret_cast<const uint8_t *>(p.v);
+        kv.table = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+        kv.kh = kh;
+        kv.KH = pl.KH;
+        kv.log2_bs = p.log2_block_size;
+        kv.max_block = p.num_blocks - 1;
+    } else {
+        const int64_t kvrow = ((int64_t)b * pl.KH + kh) * p.kv_stride;
+        kv.kbase = reinterpret_cast<const uint8_t *>(p.k) + kvrow * HSZ * (FP8 ? 1 : 2);
+        kv.vbase = reinterpret_cast<const uint8_t *>(p.v) + kvrow * HSZ * (FP8 ? 1 : 2);
+        kv.table = nullptr;
+        kv.kh = kv.KH = kv.log2_bs = kv.max_block = 0;
+    }
+    return kv;
+}
+
+// Piece fields are the same on every lane; reading them out of lane 0 keeps
+// them in scalar registers (values loaded from LDS land in vector registers).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint64_t u = (uint64_t)x;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ LeanPiece uniform_piece(const LeanPiece &x) {
+    LeanPiece u;
+    u.b = __builtin_amdgcn_readfirstlane(x.b);
+    u.kh = __builtin_amdgcn_readfirstlane(x.kh);
+    u.seg_begin = uniform64(x.seg_begin);
+    u.seg_end = uniform64(x.seg_end);
+    u.tile_begin = uniform64(x.tile_begin);
+    u.tile_end = uniform64(x.tile_end);
+    u.key_begin = __builtin_amdgcn_readfirstlane(x.key_begin);
+    u.key_end = __builtin_amdgcn_readfirstlane(x.key_end);
+    return u;
+}
+
+__device__ __forceinline__ int piece_blocks(const LeanPiece &pc) {
+    return (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
+}
+
 template <int HSZ, bool FP8, bool PAGED>
 __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
     using C = DecodeCfg<HSZ>;
@@ -420,20 +468,13 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     float *sm_o = smem + 2 * W * 16;  // [W/2][G][OSTRIDE]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: block indices stay scalar
     const int col = lane & 15;  // head g (Q, P, O), key row (K, V) or d (V^T)
     const int grp = lane >> 4;  // 8-wide slice of the MFMA contraction
     const int c = blockIdx.x;
     const int G = p.G, NC = p.NC;
     const float NEG_INF = -__builtin_inff();
     uint16_t *stage = stages + wave * C::STAGE;
-
-    // 0/1 selection operands: sel[h] picks d = 16h + col out of a 32-d chunk.
-    bf16x8 sel[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sel[h][i] = (__bf16)((8 * grp + i == 16 * h + col) ? 1.0f : 0.0f);
 
     __shared__ int merge_flag;
     __shared__ int blk_next;  // next unclaimed 32-key block of the current piece
@@ -451,6 +492,26 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     }
     const LeanPlan &pl = plan_lds;
 
+    // The first piece's first blocks are requested before any other set-up:
+    // every wave's start-up instructions then run while they are in flight.
+    int64_t t = plan_cta_begin(pl, c);
+    const int64_t t_end = plan_cta_begin(pl, c + 1);
+    Staged<HSZ, FP8> st;
+    LeanPiece pc0 = {};
+    if (t < t_end) {
+        pc0 = uniform_piece(plan_piece_at(pl, t, t_end));
+        if (wave < piece_blocks(pc0))
+            load_block<HSZ, FP8, PAGED>(st, piece_rows<HSZ, FP8, PAGED>(p, pl, pc0.b, pc0.kh),
+                                        pc0.key_begin + wave * kKeysPerBlock, pc0.key_end - 1, lane);
+    }
+
+    // 0/1 selection operands: sel[h] picks d = 16h + col out of a 32-d chunk.
+    bf16x8 sel[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sel[h][i] = (__bf16)((8 * grp + i == 16 * h + col) ? 1.0f : 0.0f);
+
     // Requests with an empty context own no tiles: their output rows are zero.
     for (int b = c; b < pl.B; b += pl.P) {
         if (pl.seqlen[b] != 0) continue;
@@ -459,24 +520,10 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             reinterpret_cast<f32x4 *>(orow)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    int64_t t = plan_cta_begin(pl, c);
-    const int64_t t_end = plan_cta_begin(pl, c + 1);
+    bool first_piece = true;
     while (t < t_end) {
-        const LeanPiece pc = plan_piece_at(pl, t, t_end);
-        KvRows<PAGED> kv;
-        if constexpr (PAGED) {
-            kv.kbase = reinterpret_cast<const uint8_t *>(p.k);
-            kv.vbase = reinterpret_cast<const uint8_t *>(p.v);
-            kv.table = p.block_table + (int64_t)pc.b * p.max_blocks_per_seq;
-            kv.kh = pc.kh;
-            kv.KH = pl.KH;
-            kv.log2_bs = p.log2_block_size;
-            kv.max_block = p.num_blocks - 1;
-        } else {
-            const int64_t kvrow = ((int64_t)pc.b * pl.KH + pc.kh) * p.kv_stride;
-            kv.kbase = reinterpret_cast<const uint8_t *>(p.k) + kvrow * HSZ * (FP8 ? 1 : 2);
-            kv.vbase = reinterpret_cast<const uint8_t *>(p.v) + kvrow * HSZ * (FP8 ? 1 : 2);
-        }
+        const LeanPiece pc = first_piece ? pc0 : uniform_piece(plan_piece_at(pl, t, t_end));
+        const KvRows<PAGED> kv = piece_rows<HSZ, FP8, PAGED>(p, pl, pc.b, pc.kh);
         const int h0 = pc.kh * G;
 
         bf16x8 qop[NS];
@@ -495,7 +542,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
 #pragma unroll
         for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const int nblk = (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
+        const int nblk = piece_blocks(pc);
         const int klast = pc.key_end - 1;
         // drafted token t (column col) sees keys up to L_b - qlen + t
         const int climit = pl.seqlen[pc.b] - p.qlen + ccol / G;
@@ -506,9 +553,9 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         // about one block of each other.  The claimed block is loading while
         // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
-        Staged<HSZ, FP8> st;
         int blk = wave;
-        if (blk < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        if (!first_piece && blk < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        first_piece = false;
         while (blk < nblk) {
             store_block<HSZ, FP8>(st, stage, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -58,13 +58,23 @@ struct LeanPlan {
     int32_t tile_prefix[ATTN_MAX_BATCH + 1];  // tiles before batch b (all its kv heads)
 };
 
+// floor(a * b / d) for integers with 0 <= a * b < 2^53 and d > 0.  The double
+// quotient is the correctly rounded x / d of an exactly represented x = a * b;
+// when x / d is not an integer it lies at least 1/d below the next integer,
+// while the rounding error is at most (x / d) * 2^-53 < 1/d, so the floor is
+// exact.  This replaces 64-bit integer division, which the GPU runs as a long
+// dependent instruction sequence, on the kernels' start-up path.
+ATTN_HD int64_t plan_muldiv(int64_t a, int64_t b, int64_t d) {
+    return (int64_t)__builtin_floor((double)(a * b) / (double)d);
+}
+
 ATTN_HD int plan_tiles_per_segment(const LeanPlan &p, int b) {
     return (p.tile_prefix[b + 1] - p.tile_prefix[b]) / p.KH;
 }
 
 // First tile of CTA c; plan_cta_begin(p, P) == N.
 ATTN_HD int64_t plan_cta_begin(const LeanPlan &p, int c) {
-    if (p.mode == kPlanStreamK) return (int64_t)c * p.N / p.P;
+    if (p.mode == kPlanStreamK) return plan_muldiv(c, p.N, p.P);  // c N < 2^12 2^31
     const int s = c / p.splits, j = c % p.splits;
     if (s >= p.B * p.KH) return p.N;
     const int b = s / p.KH, kh = s % p.KH;
@@ -73,21 +83,21 @@ ATTN_HD int64_t plan_cta_begin(const LeanPlan &p, int c) {
     const int chunks = n < p.splits ? n : p.splits;
     if (chunks == 0) return seg_begin;
     const int jj = j < chunks ? j : chunks;
-    return seg_begin + (int64_t)jj * n / chunks;
+    return seg_begin + plan_muldiv(jj, n, chunks);
 }
 
 ATTN_HD int plan_batch_of_tile(const LeanPlan &p, int64_t t);
 
 // CTA whose range contains tile t (0 <= t < N).
 ATTN_HD int plan_cta_of_tile(const LeanPlan &p, int64_t t) {
-    if (p.mode == kPlanStreamK) return (int)(((t + 1) * p.P - 1) / p.N);  // largest c with floor(cN/P) <= t
+    if (p.mode == kPlanStreamK) return (int)plan_muldiv((t + 1) * p.P - 1, 1, p.N);  // largest c with floor(cN/P) <= t
     const int b = plan_batch_of_tile(p, t);
     const int n = plan_tiles_per_segment(p, b);
-    const int64_t local = t - p.tile_prefix[b];
-    const int kh = (int)(local / n);
-    const int64_t u = local - (int64_t)kh * n;
+    const int local = (int)(t - p.tile_prefix[b]);
+    const int kh = local / n;
+    const int u = local - kh * n;
     const int chunks = n < p.splits ? n : p.splits;
-    const int j = (int)(((u + 1) * chunks - 1) / n);  // largest j with floor(j n / chunks) <= u
+    const int j = (int)plan_muldiv((int64_t)(u + 1) * chunks - 1, 1, n);  // largest j with floor(j n / chunks) <= u
     return (b * p.KH + kh) * p.splits + j;
 }
 
@@ -113,8 +123,8 @@ ATTN_HD LeanPiece plan_piece_at(const LeanPlan &p, int64_t t, int64_t cta_end) {
     LeanPiece pc;
     pc.b = plan_batch_of_tile(p, t);
     int nb = plan_tiles_per_segment(p, pc.b);
-    int64_t local = t - p.tile_prefix[pc.b];
-    pc.kh = (int)(local / nb);
+    const int local = (int)(t - p.tile_prefix[pc.b]);  // tiles fit in 31 bits
+    pc.kh = local / nb;
     pc.seg_begin = p.tile_prefix[pc.b] + (int64_t)pc.kh * nb;
     pc.seg_end = pc.seg_begin + nb;
     pc.tile_begin = t;

@@ -214,8 +214,8 @@ int attn_prefill_causal(const void *q, const void *k, const void *v, int B, int 
  *   cta_tile_begin  int64 [P+1]   CTA c owns global tiles [begin[c], begin[c+1])
  *   seg_tile_begin  int64 [B*KH+1] segment s = b*KH + kh owns tiles
  *                                  [seg_tile_begin[s], seg_tile_begin[s+1])
- * `num_ctas` must be > 0 here; the effective P is min(num_ctas, N) and is
- * written to *P_out.
+ * `num_ctas` must be in [1, ATTN_MAX_CTAS] here; the effective P is
+ * min(num_ctas, N) and is written to *P_out.
  */
 int attn_decode_plan(const int32_t *seqlens, int B, int KH, int tile_keys, int num_ctas,
                      int64_t *N_out, int *P_out, int64_t *cta_tile_begin, int64_t *seg_tile_begin);

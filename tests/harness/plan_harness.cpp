@@ -31,6 +31,26 @@ static LeanPlan make_plan(const int32_t *seqlens, int B, int KH, int T, int P, i
     return p;
 }
 
+// The kernels' exact floor(a b / d) and the stream-K range functions on a plan
+// of N tiles over P CTAs (only N, P and the mode matter to them).
+int64_t harness_muldiv(int64_t a, int64_t b, int64_t d) { return plan_muldiv(a, b, d); }
+
+static LeanPlan streamk_plan(int64_t N, int P) {
+    LeanPlan p = {};
+    p.B = 1;
+    p.KH = 1;
+    p.T = 1;
+    p.N = N;
+    p.P = P;
+    p.mode = kPlanStreamK;
+    p.splits = 1;
+    return p;
+}
+
+int64_t harness_cta_begin(int64_t N, int P, int c) { return plan_cta_begin(streamk_plan(N, P), c); }
+
+int harness_cta_of_tile(int64_t N, int P, int64_t t) { return plan_cta_of_tile(streamk_plan(N, P), t); }
+
 // rows of 8 int64: cta, b, kh, tile_begin, tile_end, key_begin, key_end, slot (-1 = whole segment)
 int64_t harness_pieces(const int32_t *seqlens, int B, int KH, int T, int P, int splits, int64_t *rows,
                        int64_t max_rows) {

@@ -30,6 +30,12 @@ def harness(tmp_path_factory):
     lib.harness_merge_tree.restype = ctypes.c_int
     lib.harness_merge_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
+    lib.harness_muldiv.restype = ctypes.c_int64
+    lib.harness_muldiv.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.harness_cta_begin.restype = ctypes.c_int64
+    lib.harness_cta_begin.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    lib.harness_cta_of_tile.restype = ctypes.c_int
+    lib.harness_cta_of_tile.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64]
     lib.harness_merge_slots.restype = ctypes.c_int
     lib.harness_merge_slots.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
@@ -198,3 +204,50 @@ def test_merge_tree_covers_every_partial_once(harness, k):
 def test_merge_tree_depth_bound():
     # kMaxCtas partials of one head need exactly kMergeLevels levels of fan-in 16
     assert MERGE_FAN_IN ** MERGE_LEVELS == MAX_CTAS
+
+
+# ------------------------------------------------- exact integer arithmetic limits
+
+def test_muldiv_is_exact_floor(harness):
+    """floor(a b / d) through a double quotient equals exact integer division on the whole
+    domain the planner uses (a b < 2^53): random draws, and numerators one below, at and
+    one above a multiple of d, where a rounding error would show."""
+    rng = np.random.default_rng(7)
+    cases = []
+    for _ in range(20000):
+        d = int(rng.integers(1, 1 << 31))
+        x = int(rng.integers(0, 1 << 53))
+        cases.append((x, 1, d))
+    for _ in range(20000):
+        d = int(rng.integers(1, 1 << 31))
+        k = int(rng.integers(0, ((1 << 53) - 2) // d))
+        for x in (k * d - 1, k * d, k * d + 1):
+            if 0 <= x < (1 << 53):
+                cases.append((x, 1, d))
+    for _ in range(20000):  # the stream-K form c * N / P
+        P = int(rng.integers(1, 4097))
+        N = int(rng.integers(1, 1 << 31))
+        cases.append((int(rng.integers(0, P + 1)), N, P))
+    for a, b, d in cases:
+        assert harness.harness_muldiv(a, b, d) == (a * b) // d, (a, b, d)
+
+
+@pytest.mark.parametrize("N", [(1 << 31) - 1, (1 << 31) - 2, 1_000_000_007, 4097, 4096])
+@pytest.mark.parametrize("P", [4096, 4095, 977, 3, 1])
+def test_stream_k_ranges_at_the_limits(harness, N, P):
+    """CTA c's first tile is floor(c N / P) and the owner of tile t is the largest c with
+    floor(c N / P) <= t, at N near 2^31 tiles and P up to the CTA limit."""
+    if P > N:
+        return
+    rng = np.random.default_rng(N % 1000 + P)
+    cs = sorted({0, 1, P - 1, P, *map(int, rng.integers(0, P + 1, 50))})
+    for c in cs:
+        assert harness.harness_cta_begin(N, P, c) == c * N // P, c
+    ts = {0, N - 1}
+    for c in cs[:-1]:
+        b = c * N // P
+        ts.update(x for x in (b - 1, b, b + 1) if 0 <= x < N)
+    ts.update(map(int, rng.integers(0, N, 50)))
+    for t in sorted(ts):
+        c = harness.harness_cta_of_tile(N, P, t)
+        assert c * N // P <= t < (c + 1) * N // P, (t, c)
