@@ -24,16 +24,14 @@
 //      with the head index on lanes and four consecutive keys per lane;
 //   3. online softmax in the log2 domain; the row max over the block needs two
 //      cross-lane steps (lanes 16 and 32 apart);
-//   4. V^T by MFMA: a product with a 0/1 selection matrix re-distributes a
-//      16-key x 32-d tile of V so that each lane holds four consecutive keys of
-//      one d (exact: one product by 1.0 plus zeros);
+//   4. V^T straight from the row-major V stage: transposing LDS reads
+//      (ds_read_b64_tr_b16) hand each lane four consecutive keys of one d;
 //   5. BMM2 on MFMA with A = V^T (16 d x 32 keys), B = P^T (32 keys x 16 heads);
 //      P is split into bf16 hi + lo parts (two MFMAs), so the weights keep
 //      ~2^-17 relative accuracy instead of bf16's 2^-9.
 //  The key order inside each MFMA contraction is chosen so that the lanes that
-//  hold S^T after step 2 already hold the P^T operand of step 5 and the lanes
-//  of step 4's output already hold the V^T operand: no shuffles beyond the two
-//  row-max steps.  At the end of a piece the wave states are merged through
+//  hold S^T after step 2 already hold the P^T operand of step 5, and step 4
+//  reads V^T in that same key order: no shuffles beyond the two row-max steps.  At the end of a piece the wave states are merged through
 //  LDS (max, rescale, tree sum) and written either as the final output or,
 //  when the head is split over several CTAs, as a partial slot.  The CTA that
 //  arrives last at a split head (one atomic counter per group) merges the
@@ -52,6 +50,19 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, con
 
 __device__ __forceinline__ bf16x8 load_row8(const uint16_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Four keys of one d column of a row-major bf16 LDS stage with row stride rs:
+// within each 16-lane block, lane t reads 8 bytes at row key0 + t/4, columns
+// d0 + 4 (t % 4) .. +3, and the transposing read (ds_read_b64_tr_b16) hands
+// lane i the column d0 + i at rows key0 .. key0 + 3.
+__device__ __forceinline__ i16x4 v_cols(const uint16_t *stage, int rs, int key0, int d0, int t) {
+    const uint16_t *p = stage + (key0 + (t >> 2)) * rs + d0 + 4 * (t & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
 }
 
 __device__ __forceinline__ float wave_max_over_groups(float x) {
@@ -183,7 +194,7 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterp
 // are masked.
 template <int HSZ>
 __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[HSZ / 32],
-                                              const bf16x8 (&sel)[2], int key0, int kmax, int col, int grp,
+                                              int key0, int kmax, int col, int grp,
                                               float scale_log2, float &m_run, float &l_run,
                                               f32x4 (&oacc)[HSZ / 16]) {
     using C = DecodeCfg<HSZ>;
@@ -191,7 +202,6 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
     constexpr int ND = C::ND;
     const float NEG_INF = -__builtin_inff();
     const uint16_t *krow = stage + col * C::RS + 8 * grp;                        // key col of 16-key block 0
-    const uint16_t *vrow = stage + (kKeysPerBlock + col) * C::RS + 8 * grp;
     // BMM1: S^T[key][g] for keys key0 + 16kb + 4grp + i in lane (g = col, grp)
     f32x4 sc[2];
 #pragma unroll
@@ -230,26 +240,18 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
     m_run = m_new;
 #pragma unroll
     for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-    // V^T via selection MFMAs, then BMM2 with the hi and lo parts of P
+    // BMM2: the Vᵀ operand comes straight out of the row-major V stage through
+    // transposing reads.  Lane (i, grp) gets V[4 grp + j][16 db + i] and
+    // V[16 + 4 grp + j][16 db + i], j = 0..3: the key order of this lane's Sᵀ
+    // accumulator, so P needs no shuffle.  P enters as its bf16 hi and lo parts.
+    const uint16_t *vstage = stage + kKeysPerBlock * C::RS;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const bf16x8 v0 = lds_row8(vrow + 32 * s);
-        const bf16x8 v1 = lds_row8(vrow + 16 * C::RS + 32 * s);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 t0 = mfma_bf16(v0, sel[h], z);
-            const f32x4 t1 = mfma_bf16(v1, sel[h], z);
-            bf16x8 vt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vt[i] = (__bf16)t0[i];
-                vt[4 + i] = (__bf16)t1[i];
-            }
-            const int db = 2 * s + h;
-            oacc[db] = mfma_bf16(vt, phi, oacc[db]);
-            oacc[db] = mfma_bf16(vt, plo, oacc[db]);
-        }
+    for (int db = 0; db < ND; ++db) {
+        const i16x4 a = v_cols(vstage, C::RS, 4 * grp, 16 * db, col);
+        const i16x4 b = v_cols(vstage, C::RS, 16 + 4 * grp, 16 * db, col);
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = mfma_bf16(vt, phi, oacc[db]);
+        oacc[db] = mfma_bf16(vt, plo, oacc[db]);
     }
 }
 
@@ -505,13 +507,6 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
                                         pc0.key_begin + wave * kKeysPerBlock, pc0.key_end - 1, lane);
     }
 
-    // 0/1 selection operands: sel[h] picks d = 16h + col out of a 32-d chunk.
-    bf16x8 sel[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sel[h][i] = (__bf16)((8 * grp + i == 16 * h + col) ? 1.0f : 0.0f);
-
     // Requests with an empty context own no tiles: their output rows are zero.
     for (int b = c; b < pl.B; b += pl.P) {
         if (pl.seqlen[b] != 0) continue;
@@ -565,7 +560,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ>(stage, qop, sel, pc.key_begin + blk * kKeysPerBlock, kmax, col, grp, p.scale_log2,
+            process_block<HSZ>(stage, qop, pc.key_begin + blk * kKeysPerBlock, kmax, col, grp, p.scale_log2,
                                m_run, l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
