@@ -23,7 +23,7 @@ ATTN_ERR_HIP = -6
 ATTN_MAX_BATCH = 256
 ATTN_MAX_GROUP = 16
 ATTN_MAX_CTAS = 4096
-ATTN_DECODE_COUNTER_BYTES = 98304
+ATTN_DECODE_COUNTER_BYTES = 32768
 ATTN_SCHEDULE_AUTO = 0
 ATTN_SCHEDULE_STREAM_K = 1
 ATTN_SCHEDULE_FIXED_SPLIT = 2

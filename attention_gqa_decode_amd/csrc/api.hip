@@ -145,16 +145,31 @@ int default_splits(const LeanPlan &p, int resident) {
     return S < 1 ? 1 : S;
 }
 
-bool any_split_segment(const LeanPlan &p) {
+// One pass over the segments: whether any of them is split over several CTAs
+// (*split), and the list of those split over more than kMergeFanIn CTAs (their
+// merge runs in merge_wide_kernel).  Each such head owns the whole ranges of
+// at least kMergeFanIn - 1 CTAs, so there are at most kMaxWideHeads of them;
+// returns false if the list would still overflow.
+bool scan_segments(const LeanPlan &p, bool *split, attn::WideMergeParams *wide) {
+    *split = false;
+    wide->count = 0;
     for (int b = 0; b < p.B; ++b) {
         const int nb = plan_tiles_per_segment(p, b);
         if (nb == 0) continue;
         for (int kh = 0; kh < p.KH; ++kh) {
             const int64_t s0 = p.tile_prefix[b] + (int64_t)kh * nb;
-            if (plan_cta_of_tile(p, s0) != plan_cta_of_tile(p, s0 + nb - 1)) return true;
+            const int n = plan_segment_ctas(p, s0, s0 + nb).n;
+            *split |= n > 1;
+            if (n > attn::kMergeFanIn) {
+                if (wide->count == attn::kMaxWideHeads) return false;
+                const int c_lo = plan_cta_of_tile(p, s0);
+                attn::WideHead &h = wide->head[wide->count++];
+                h.bkh = b | kh << 8;
+                h.cta = c_lo | (n - 1) << 12 | (plan_slot(p, c_lo, s0) & 1) << 24;
+            }
         }
     }
-    return false;
+    return true;
 }
 
 }  // namespace
@@ -304,7 +319,13 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.plan.P = P;
     p.counters = nullptr;
 
-    if (p.plan.N > 0 && any_split_segment(p.plan)) {
+    attn::WideMergeParams wide;
+    wide.count = 0;
+    bool split = false;
+    if (p.plan.N > 0 && !scan_segments(p.plan, &split, &wide))
+        return fail(ATTN_ERR_UNSUPPORTED, "more than %d heads split over more than %d workgroups", attn::kMaxWideHeads,
+                    attn::kMergeFanIn);
+    if (split) {
         const size_t need = attn::decode_workspace_bytes(P, p.NC, a->Hsz);
         char *w = nullptr;
         if (a->workspace) {
@@ -328,6 +349,18 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
     if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
         return fail_hip(e, "hipEventRecord(end)");
+    if (p.ws && wide.count > 0) {
+        wide.ws = p.ws;
+        wide.out = p.out;
+        wide.slot_floats = p.slot_floats;
+        wide.NC = p.NC;
+        wide.G = p.G;
+        wide.Hq = p.Hq;
+        wide.qlen = p.qlen;
+        wide.v_scale = p.v_scale;
+        e = attn::launch_merge_wide(wide, a->Hsz, stream);
+        if (e != hipSuccess) return fail_hip(e, "wide merge kernel launch");
+    }
     return ATTN_OK;
 }
 

@@ -24,7 +24,7 @@ struct DecodeParams {
     const uint16_t *v;   // same layout as k
     float *out;          // fp32 [B][Hq][Hsz]
     float *ws;           // partial slots, each slot_floats long
-    int *counters;       // arrival counters [kMergeLevels][2 * kMaxCtas], zero between calls
+    int *counters;       // arrival counters [2 * kMaxCtas], zero between calls
     int64_t kv_stride;   // S
     int Hq;
     int G;
@@ -43,22 +43,41 @@ struct DecodeParams {
 // Partial slot layout: O[NC][Hsz] unnormalised, then m[NC] (log2 domain), then l[NC].
 inline int decode_slot_floats(int NC, int Hsz) { return (NC * Hsz + 2 * NC + 3) & ~3; }
 
-// Split heads are merged inside the tile kernel by a tree of fan-in kMergeFanIn:
-// the last CTA to arrive at a group merges it.  kMergeLevels levels cover
-// kMergeFanIn^kMergeLevels = kMaxCtas partials of one head.
+// Split heads whose partials sit in at most kMergeFanIn CTAs are merged inside
+// the tile kernel by the CTA that arrives last; wider heads (at most
+// kMaxWideHeads of them: each one has at least kMergeFanIn - 1 CTAs to
+// itself) by merge_wide_kernel.
 constexpr int kMergeFanIn = 16;
-constexpr int kMergeLevels = 3;
 constexpr int kMaxCtas = 4096;
+constexpr int kMaxWideHeads = (kMaxCtas + kMergeFanIn - 2) / (kMergeFanIn - 1);
 
-// Workspace layout: int counters[kMergeLevels][2 * kMaxCtas] (a fixed-size
-// region, so its place never depends on P), then float slots[2P][slot_floats].
-constexpr size_t kCounterBytes = (size_t)kMergeLevels * 2 * kMaxCtas * sizeof(int);
+// A wide head for merge_wide_kernel, packed so one scalar load fetches it:
+// bkh = b | kh << 8; cta = c_lo | (n - 1) << 12 | (slot of partial 0 is odd) << 24.
+struct WideHead {
+    int32_t bkh;
+    int32_t cta;
+};
+
+struct WideMergeParams {
+    const float *ws;      // partial slots
+    float *out;           // fp32 [B][Hq][qlen][Hsz]
+    int slot_floats;
+    int NC, G, Hq, qlen;
+    float v_scale;
+    int count;            // wide heads
+    WideHead head[kMaxWideHeads];
+};
+
+// Workspace layout: int counters[2 * kMaxCtas] (a fixed-size region, so its
+// place never depends on P), then float slots[2P][slot_floats].
+constexpr size_t kCounterBytes = (size_t)2 * kMaxCtas * sizeof(int);
 inline size_t decode_workspace_bytes(int P, int NC, int Hsz) {
     return kCounterBytes + (size_t)2 * P * decode_slot_floats(NC, Hsz) * sizeof(float);
 }
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream);
+hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int NC);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave

@@ -33,12 +33,14 @@
 //  hold S^T after step 2 already hold the P^T operand of step 5, and step 4
 //  reads V^T in that same key order: no shuffles beyond the two row-max steps.  At the end of a piece the wave states are merged through
 //  LDS (max, rescale, tree sum) and written either as the final output or,
-//  when the head is split over several CTAs, as a partial slot.  The CTA that
-//  arrives last at a split head (one atomic counter per group) merges the
-//  partials by rescaling them to their common max: directly when the head has
-//  at most 16 partials, otherwise through a tree of fan-in 16 whose inner
-//  nodes are written back into partial slots.  No CTA ever waits for another,
-//  so the merge needs no co-residency, and there is no second kernel launch.
+//  when the head is split over several CTAs, as a partial slot.  A head split
+//  over at most 16 CTAs is merged by the CTA that arrives last at its atomic
+//  counter, which rescales the partials to their common max.  A wider head is
+//  merged by merge_wide_kernel, launched next on the stream: one CU reads only
+//  about 20-30 GB/s of freshly written partials, so a single merging CTA (or a
+//  tree of them) would sit on the critical path for microseconds, while the
+//  merge kernel reads them with one workgroup per 16 output columns.  No CTA
+//  ever waits for another, so neither merge needs co-residency.
 #include "common.h"
 
 namespace attn {
@@ -301,109 +303,151 @@ __device__ __forceinline__ int partial_slot(const LeanPlan &pl, int c_lo, int64_
 
 // Called by every thread of CTA c right after it wrote its partial of the split
 // segment (b, kh) into its slot (each writing wave has waited for its stores).
-// Arrives at the counter of its merge group; the last arrival merges the group
-// (up to kMergeFanIn states) and either writes the final output (top of the
-// tree) or an inner state into the group's first slot and climbs one level.
+// A head whose partials sit in at most kMergeFanIn CTAs is merged here: the
+// CTA that arrives last at the head's counter reads every partial, rescales
+// them to their common max and writes the output.  Wider heads are left to
+// merge_wide_kernel, which reads their partials with many workgroups at once.
 // All control flow is uniform over the CTA.
 template <int HSZ, int NT>
-__device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPiece &pc, int c, int *flag) {
+__device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPiece &pc, int *flag) {
     const int NC = p.NC, G = p.G;
     const int tid = threadIdx.x;
-    const int nb = (int)(pc.seg_end - pc.seg_begin);
-    const int c_lo = plan_cta_of_tile(pl, pc.seg_begin);
-    const int k = plan_cta_of_tile(pl, pc.seg_begin + nb - 1) - c_lo + 1;  // partials of this head
-    int i = c - c_lo;  // index of the state this CTA carries up the tree
-    int span = 1;      // partials covered by one state at the current level
+    const SegmentCtas sc = plan_segment_ctas(pl, pc.seg_begin, pc.seg_end);
+    const int c_lo = sc.c_lo, n = sc.n;  // partials of this head
+    if (n > kMergeFanIn) return;
+    __syncthreads();  // every wave's slot stores have completed
+    if (tid == 0) {
+        int *cnt = p.counters + partial_slot(pl, c_lo, pc.seg_begin, 0);
+        const int old = atomicAdd(cnt, 1);
+        const int last = old == n - 1;
+        if (last) atomicExch(cnt, 0);  // counters are zero again for the next call
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
     constexpr int UNITS = kMaxGroup * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound (NC <= 16)
-    for (int level = 0; level < kMergeLevels; ++level) {
-        const MergeGroup mg = plan_merge_group(k, i, span, kMergeFanIn);
-        const int first = mg.first, n = mg.n;
-        const bool top = mg.root;
-        if (n > 1) {
-            __syncthreads();  // every wave's slot stores have completed
-            if (tid == 0) {
-                int *cnt = p.counters + level * 2 * kMaxCtas + partial_slot(pl, c_lo, pc.seg_begin, first * span);
-                const int old = atomicAdd(cnt, 1);
-                const int last = old == n - 1;
-                if (last) atomicExch(cnt, 0);  // counters are zero again for the next call
-                *flag = last;
-            }
-            __syncthreads();
-            if (!*flag) return;
-        } else if (!top) {
-            span *= kMergeFanIn;  // a group of one: its state already sits in place
-            continue;
-        }
-        // merge states first .. first+n-1 of this level
-        const int units = NC * HSZ / 4;
-        f32x4 res[UNITS];
-        float Lsum[UNITS], Mmax[UNITS];
+    const int units = NC * HSZ / 4;
 #pragma unroll
-        for (int r = 0; r < UNITS; ++r) {
-            const int u = tid + r * NT;
-            res[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Lsum[r] = 0.f;
-            Mmax[r] = -__builtin_inff();
-            if (u >= units) continue;
-            const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
-            float mv[kMergeFanIn], lv[kMergeFanIn];
-            f32x4 ov[kMergeFanIn];
+    for (int r = 0; r < UNITS; ++r) {
+        const int u = tid + r * NT;
+        if (u >= units) continue;
+        const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
+        float mv[kMergeFanIn], lv[kMergeFanIn];
+        f32x4 ov[kMergeFanIn];
 #pragma unroll
-            for (int j = 0; j < kMergeFanIn; ++j) {
-                mv[j] = -__builtin_inff();
-                lv[j] = 0.f;
-                ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (j < n) {
-                    const float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, (first + j) * span) * p.slot_floats;
-                    mv[j] = ld_shared_f(sp + NC * HSZ + g);
-                    lv[j] = ld_shared_f(sp + NC * HSZ + NC + g);
-                    ov[j] = ld_shared_f4(sp + g * HSZ + 4 * d4);
-                }
-            }
-            float M = mv[0];
-#pragma unroll
-            for (int j = 1; j < kMergeFanIn; ++j) M = fmaxf(M, mv[j]);
-            // M is -inf only for a drafted token whose limit lies before every member's keys
-            const float Muse = M == -__builtin_inff() ? 0.f : M;
-            float L = 0.f;
-            f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < kMergeFanIn; ++j) {
-                const float f = j < n ? __builtin_amdgcn_exp2f(mv[j] - Muse) : 0.f;
-                L += lv[j] * f;
-                O += ov[j] * f;
-            }
-            res[r] = O;
-            Lsum[r] = L;
-            Mmax[r] = M;
-        }
-        if (top) {
-#pragma unroll
-            for (int r = 0; r < UNITS; ++r) {
-                const int u = tid + r * NT;
-                if (u >= units) continue;
-                const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);  // column g: token g / G, head g % G
-                float *dst = p.out + (((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
-                *reinterpret_cast<f32x4 *>(dst) = res[r] * (p.v_scale / Lsum[r]);
-            }
-            return;
-        }
-        __syncthreads();  // every member state is read before the first slot is overwritten
-        float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, first * span) * p.slot_floats;
-#pragma unroll
-        for (int r = 0; r < UNITS; ++r) {
-            const int u = tid + r * NT;
-            if (u >= units) continue;
-            const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
-            st_shared_f4(sp + g * HSZ + 4 * d4, res[r]);
-            if (d4 == 0) {
-                st_shared_f(sp + NC * HSZ + g, Mmax[r]);
-                st_shared_f(sp + NC * HSZ + NC + g, Lsum[r]);
+        for (int j = 0; j < kMergeFanIn; ++j) {
+            mv[j] = -__builtin_inff();
+            lv[j] = 0.f;
+            ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < n) {
+                const float *sp = p.ws + (int64_t)partial_slot(pl, c_lo, pc.seg_begin, j) * p.slot_floats;
+                mv[j] = ld_shared_f(sp + NC * HSZ + g);
+                lv[j] = ld_shared_f(sp + NC * HSZ + NC + g);
+                ov[j] = ld_shared_f4(sp + g * HSZ + 4 * d4);
             }
         }
-        wait_memory();
-        i = first * span;
-        span *= kMergeFanIn;
+        float M = mv[0];
+#pragma unroll
+        for (int j = 1; j < kMergeFanIn; ++j) M = fmaxf(M, mv[j]);
+        // M is -inf only for a drafted token whose limit lies before every member's keys
+        const float Muse = M == -__builtin_inff() ? 0.f : M;
+        float L = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMergeFanIn; ++j) {
+            const float f = j < n ? __builtin_amdgcn_exp2f(mv[j] - Muse) : 0.f;
+            L += lv[j] * f;
+            O += ov[j] * f;
+        }
+        // column g: token g / G, head g % G
+        float *dst = p.out + (((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
+        *reinterpret_cast<f32x4 *>(dst) = O * (p.v_scale / L);
+    }
+}
+
+// (M, L, O) <- the rescaled sum of two partial states of one column; an empty
+// state has M = -inf and contributes nothing.
+__device__ __forceinline__ void combine_state(float &M, float &L, f32x4 &O, float M2, float L2, const f32x4 &O2) {
+    const float Mn = fmaxf(M, M2);
+    const float f1 = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float f2 = M2 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M2 - Mn);
+    L = L * f1 + L2 * f2;
+    O = O * f1 + O2 * f2;
+    M = Mn;
+}
+
+// Merge of the heads whose partials sit in more than kMergeFanIn CTAs (long
+// contexts over few kv heads), launched after the tile kernel.  Workgroup
+// (x, y) takes columns [16x, 16x + 16) of the NC x HSZ state of wide head y:
+// thread t covers float4 column t % 4 over the partials t / 4, t / 4 + 64, ...
+// (online rescaling), then the 64 threads of each column combine their states
+// through lane shuffles and LDS.  The same rescaled sum as the in-kernel merge
+// ("LeanAttention" digest, section "조각별로 합칠 수 있는 정확한 소프트맥스"),
+// spread over many CUs instead of read by the one CTA that arrives last.
+template <int HSZ>
+__global__ __launch_bounds__(256) void merge_wide_kernel(const WideMergeParams mp) {
+    const WideHead hd = mp.head[blockIdx.y];
+    const int b = hd.bkh & 255, kh = hd.bkh >> 8;
+    const int c_lo = hd.cta & 4095, n = ((hd.cta >> 12) & 4095) + 1;
+    const int slot0 = 2 * c_lo + (hd.cta >> 24);
+    const int NC = mp.NC, G = mp.G;
+    const int g = blockIdx.x * 16 / HSZ;
+    const int col = blockIdx.x * 16 % HSZ + 4 * (threadIdx.x & 3);
+    const int lane_j = threadIdx.x >> 2;
+    float M = -__builtin_inff(), L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    constexpr int R = 4;  // partials per thread per round of loads
+    for (int j0 = 0; j0 < n; j0 += 64 * R) {
+        float mv[R], lv[R];
+        f32x4 ov[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int j = j0 + lane_j + 64 * r;
+            mv[r] = -__builtin_inff();
+            lv[r] = 0.f;
+            ov[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < n) {
+                const float *sp = mp.ws + (int64_t)(j == 0 ? slot0 : 2 * (c_lo + j)) * mp.slot_floats;
+                mv[r] = ld_shared_f(sp + NC * HSZ + g);
+                lv[r] = ld_shared_f(sp + NC * HSZ + NC + g);
+                ov[r] = ld_shared_f4(sp + g * HSZ + col);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) combine_state(M, L, O, mv[r], lv[r], ov[r]);
+    }
+    // the 16 partial lanes of a column within the wave: lane bits 2..5
+#pragma unroll
+    for (int sh = 4; sh < 64; sh <<= 1) {
+        const float M2 = __shfl_xor(M, sh), L2 = __shfl_xor(L, sh);
+        f32x4 O2;
+        O2[0] = __shfl_xor(O[0], sh);
+        O2[1] = __shfl_xor(O[1], sh);
+        O2[2] = __shfl_xor(O[2], sh);
+        O2[3] = __shfl_xor(O[3], sh);
+        combine_state(M, L, O, M2, L2, O2);
+    }
+    __shared__ float red[4][4][8];  // [wave][column][M, L, O0..3]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane < 4) {
+        float *r = red[wave][lane];
+        r[0] = M;
+        r[1] = L;
+        r[2] = O[0];
+        r[3] = O[1];
+        r[4] = O[2];
+        r[5] = O[3];
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int u = threadIdx.x;
+        for (int w = 1; w < 4; ++w) {
+            const float *r = red[w][u];
+            combine_state(M, L, O, r[0], r[1], f32x4{r[2], r[3], r[4], r[5]});
+        }
+        // column g: token g / G, head g % G
+        float *dst = mp.out + (((int64_t)b * mp.Hq + kh * G + g % G) * mp.qlen + g / G) * HSZ + col;
+        *reinterpret_cast<f32x4 *>(dst) = O * (mp.v_scale / L);
     }
 }
 
@@ -623,7 +667,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             }
             if (!whole) wait_memory();
         }
-        if (!whole) merge_up<HSZ, W * 64>(p, pl, pc, c, &merge_flag);
+        if (!whole) merge_up<HSZ, W * 64>(p, pl, pc, &merge_flag);
         t = pc.tile_end;
     }
 }
@@ -665,6 +709,12 @@ hipError_t launch_tiles_h(const DecodeParams &p, bool fp8, hipStream_t stream) {
 }
 
 template <int HSZ>
+hipError_t launch_merge_wide_h(const WideMergeParams &mp, hipStream_t stream) {
+    hipLaunchKernelGGL(merge_wide_kernel<HSZ>, dim3(mp.NC * HSZ / 16, mp.count), dim3(256), 0, stream, mp);
+    return hipGetLastError();
+}
+
+template <int HSZ>
 int occupancy_t(int G) {
     int blocks = 0;
     const size_t lds = decode_tiles_lds_bytes<HSZ>(G);
@@ -692,6 +742,15 @@ hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStre
         case 64: return launch_tiles_h<64>(p, fp8, stream);
         case 128: return launch_tiles_h<128>(p, fp8, stream);
         case 256: return launch_tiles_h<256>(p, fp8, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream) {
+    switch (Hsz) {
+        case 64: return launch_merge_wide_h<64>(mp, stream);
+        case 128: return launch_merge_wide_h<128>(mp, stream);
+        case 256: return launch_merge_wide_h<256>(mp, stream);
         default: return hipErrorInvalidValue;
     }
 }

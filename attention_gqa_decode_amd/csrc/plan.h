@@ -141,25 +141,18 @@ ATTN_HD int plan_slot(const LeanPlan &p, int c, int64_t seg_begin) {
     return 2 * c + (seg_begin <= plan_cta_begin(p, c) ? 0 : 1);
 }
 
-// Merge tree over the k partials of one split segment (partial i comes from
-// CTA c_lo + i).  At a level where one state covers `span` partials there are
-// ceil(k / span) states; state s belongs to the group of states
-// [first, first + n) with first = s rounded down to a multiple of fan_in.  The
-// last member to arrive at a group merges it; when the level has at most
-// fan_in states the group is the root and its merge is the final output,
-// otherwise the merged state covers partials [first*span, (first+n)*span) and
-// is stored in the slot of partial first*span.
-struct MergeGroup {
-    int first;  // first member state of the group (state units of this level)
-    int n;      // members in the group, 1..fan_in
-    bool root;  // the merge of this group is the final output
+// The CTAs c_lo .. c_lo + n - 1 hold the pieces of the segment with tiles
+// [seg_begin, seg_end) (non-empty).  n > 1 means the head is split and leaves
+// one partial in each of them: partial i sits in slot plan_slot(p, c_lo,
+// seg_begin) for i = 0 and in slot 2 (c_lo + i) otherwise.
+struct SegmentCtas {
+    int c_lo;
+    int n;
 };
 
-ATTN_HD MergeGroup plan_merge_group(int k, int i, int span, int fan_in) {
-    MergeGroup g;
-    const int states = (k + span - 1) / span;
-    g.first = (i / span) / fan_in * fan_in;
-    g.n = states - g.first < fan_in ? states - g.first : fan_in;
-    g.root = states <= fan_in;
-    return g;
+ATTN_HD SegmentCtas plan_segment_ctas(const LeanPlan &p, int64_t seg_begin, int64_t seg_end) {
+    SegmentCtas s;
+    s.c_lo = plan_cta_of_tile(p, seg_begin);
+    s.n = plan_cta_of_tile(p, seg_end - 1) - s.c_lo + 1;
+    return s;
 }

@@ -62,8 +62,9 @@ enum attn_status {
 #define ATTN_MAX_GROUP 16
 /* Largest number of persistent decode workgroups (num_ctas). */
 #define ATTN_MAX_CTAS 4096
-/* Bytes at the start of a decode workspace that hold the merge counters. */
-#define ATTN_DECODE_COUNTER_BYTES 98304
+/* Bytes at the start of a decode workspace that hold the merge counters
+ * (one arrival counter per partial slot). */
+#define ATTN_DECODE_COUNTER_BYTES 32768
 
 /*
  * attn_decode -- one decode step of GQA attention (query length 1).
@@ -81,8 +82,11 @@ enum attn_status {
  * tiles of the whole batch are numbered globally and split evenly over all
  * resident workgroups, each of which keeps the G query heads of a group
  * together.  A head split across workgroups leaves one partial (max, sum, O)
- * state per workgroup; the workgroup that finishes last merges them by
- * rescaling to the common max, inside the same kernel (one launch per call).
+ * state per workgroup, merged by rescaling to the common max.  When a head is
+ * split over at most 16 workgroups, the one that finishes last merges it
+ * inside the same kernel; heads split over more (long contexts over few kv
+ * heads) are merged by a second, short kernel on the same stream, which
+ * spreads the reading of their partials over many workgroups.
  * The library owns the partial-state buffer (one per device and stream, grown
  * on demand with hipMalloc and zero-filled on the stream, freed by
  * attn_release); calls on the same stream are ordered, calls that share a
@@ -148,7 +152,8 @@ typedef struct attn_decode_args {
     int num_ctas;             /* stream-K: number of persistent workgroups P, <= ATTN_MAX_CTAS;
                                  0 = all resident slots.  Must be 0 for the fixed split. */
     hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the decode kernel */
-    hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel */
+    hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel (before the
+                                 merge kernel of heads split over more than 16 workgroups) */
     int schedule;             /* ATTN_SCHEDULE_*; 0 = AUTO */
     int num_splits;           /* fixed split: chunks per (request, kv head); 0 = fill the GPU once.
                                  With more than one split, B*KH*num_splits <= ATTN_MAX_CTAS. */

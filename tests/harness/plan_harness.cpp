@@ -4,7 +4,6 @@
 // by tests/test_plan.py; no GPU involved.
 #include <stdint.h>
 
-#include <map>
 #include <vector>
 
 #include "../../attention_gqa_decode_amd/csrc/plan.h"
@@ -90,49 +89,27 @@ int harness_merge_slots(const int32_t *seqlens, int B, int KH, int T, int P, int
     return k;
 }
 
-// Simulates the fused merge of one split segment with k partials, fan-in F and
-// `levels` tree levels, with the CTAs arriving in `order` (a permutation of
-// 0..k-1).  Each CTA climbs exactly as the tile kernel does: at every level it
-// arrives at its group's counter (groups of one are skipped) and goes on only
-// if it was the last member; the root merge produces the output.  Every slot
-// holds the multiset of partials folded into it.  Returns the number of root
-// merges; coverage[i] counts how often partial i reached the output, and
-// *counters_left is the sum of all counters afterwards (0 = all reset).
-int harness_merge_tree(int k, int F, int levels, const int32_t *order, int32_t *coverage, int64_t *counters_left) {
-    std::vector<std::vector<int>> slot(k);
-    for (int i = 0; i < k; ++i) slot[i] = {i};
-    std::map<std::pair<int, int>, int> cnt;
-    for (int i = 0; i < k; ++i) coverage[i] = 0;
-    int roots = 0;
-    for (int a = 0; a < k; ++a) {
-        int idx = order[a], span = 1;
-        for (int level = 0; level < levels; ++level) {
-            MergeGroup g = plan_merge_group(k, idx, span, F);
-            if (g.n > 1) {
-                int &c = cnt[{level, g.first * span}];
-                if (++c != g.n) break;
-                c = 0;
-            } else if (!g.root) {
-                span *= F;
-                continue;
-            }
-            std::vector<int> merged;
-            for (int j = 0; j < g.n; ++j)
-                for (int x : slot[(g.first + j) * span]) merged.push_back(x);
-            if (g.root) {
-                ++roots;
-                for (int x : merged) ++coverage[x];
-                break;
-            }
-            slot[g.first * span] = merged;
-            idx = g.first * span;
-            span *= F;
+// For every segment s = b*KH + kh: the first CTA and the number of CTAs that
+// hold its pieces, from plan_segment_ctas (n = 0 for an empty segment).
+// Returns how many segments are split over more than `width` CTAs.
+int harness_segment_ctas(const int32_t *seqlens, int B, int KH, int T, int P, int splits, int width, int32_t *c_lo,
+                         int32_t *n) {
+    LeanPlan p = make_plan(seqlens, B, KH, T, P, splits);
+    int wide = 0;
+    for (int b = 0; b < B; ++b) {
+        const int nb = plan_tiles_per_segment(p, b);
+        for (int kh = 0; kh < KH; ++kh) {
+            const int s = b * KH + kh;
+            c_lo[s] = n[s] = 0;
+            if (nb == 0) continue;
+            const int64_t s0 = p.tile_prefix[b] + (int64_t)kh * nb;
+            const SegmentCtas sc = plan_segment_ctas(p, s0, s0 + nb);
+            c_lo[s] = sc.c_lo;
+            n[s] = sc.n;
+            wide += sc.n > width;
         }
     }
-    int64_t left = 0;
-    for (auto &kv : cnt) left += kv.second;
-    *counters_left = left;
-    return roots;
+    return wide;
 }
 }
 

@@ -100,7 +100,7 @@ def ex_args(**kw):
     (dict(scale=float("nan")), A.ATTN_ERR_SHAPE),
     (dict(workspace=FAKE + 4, workspace_bytes=1 << 20), A.ATTN_ERR_ALIGN),
     (dict(workspace=FAKE, workspace_bytes=16, num_ctas=4), A.ATTN_ERR_WORKSPACE),
-    (dict(workspace=FAKE, workspace_bytes=98304, num_ctas=4), A.ATTN_ERR_WORKSPACE),  # counters only
+    (dict(workspace=FAKE, workspace_bytes=32768, num_ctas=4), A.ATTN_ERR_WORKSPACE),  # counters only
     (dict(num_ctas=4097), A.ATTN_ERR_UNSUPPORTED),
     (dict(schedule=3), A.ATTN_ERR_SHAPE),
     (dict(schedule=-1), A.ATTN_ERR_SHAPE),
@@ -165,7 +165,7 @@ def test_plan_argument_checks():
 def test_workspace_bytes_formula():
     # the counter region, then 2 slots per CTA, each G*Hsz (O) + 2G (m, l) floats rounded up to 4
     C = A.ATTN_DECODE_COUNTER_BYTES
-    assert C == 3 * 2 * A.ATTN_MAX_CTAS * 4  # three tree levels of one counter per partial slot
+    assert C == 2 * A.ATTN_MAX_CTAS * 4  # one arrival counter per partial slot
     assert A.attn_decode_workspace_bytes(16, 32, 8, 128, 100) == C + 2 * 100 * ((4 * 128 + 8 + 3) & ~3) * 4
     assert A.attn_decode_workspace_bytes(1, 8, 1, 64, 7) == C + 2 * 7 * ((8 * 64 + 16 + 3) & ~3) * 4
     assert A.attn_decode_workspace_bytes(1, 8, 3, 64, 7) == 0  # Hq % KH != 0

@@ -97,3 +97,11 @@ def test_fp8_full_size_workloads(name):
     assert err <= DECODE_TOL
     del t
     torch.cuda.empty_cache()
+
+
+def test_fp8_wide_head():
+    # one long head split over 300 CTAs: the wide merge kernel applies the value scale
+    shape = W.DecodeShape("w", 1, 8, 1, 128, (40000,), seed=95)
+    err, _ = fp8_err(shape, k_scale=0.5, v_scale=2.0, tile_keys=64, num_ctas=300)
+    note(f"fp8 wide head: max err {err:.3e}")
+    assert err <= DECODE_TOL

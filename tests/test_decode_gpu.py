@@ -247,3 +247,50 @@ def test_fixed_split_full_size(name):
     assert err <= DECODE_TOL
     del q, k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ wide heads
+
+def ctas_per_head(sl, KH, T, P):
+    """CTAs holding a piece of each (request, kv head) under the stream-K plan."""
+    _, _, cta, seg = A.attn_decode_plan(sl, KH, T, P)
+    out = []
+    for s in range(len(sl) * KH):
+        if seg[s + 1] == seg[s]:
+            out.append(0)
+            continue
+        lo = np.searchsorted(cta, seg[s], side="right") - 1
+        hi = np.searchsorted(cta, seg[s + 1] - 1, side="right") - 1
+        out.append(int(hi - lo + 1))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("Hsz", [64, 128, 256])
+def test_wide_and_narrow_heads_in_one_call(Hsz):
+    # request 0's heads span well over 16 CTAs (merged by the wide merge kernel), request 2's
+    # a few (merged inside the tile kernel), request 1's one (finished by its CTA)
+    sl = [120000, 300, 3000, 0]
+    T, P = 128, 256
+    widths = ctas_per_head(sl, 2, T, P)
+    note(f"decode wide+narrow heads Hsz={Hsz}: CTAs per head {widths.tolist()}")
+    assert widths.max() > 16 and ((widths > 1) & (widths <= 16)).any()
+    q, k, v, sl = inputs(4, 8, 2, Hsz, sl, seed=90 + Hsz)
+    err, got = decode_err(q, k, v, sl, tile_keys=T, num_ctas=P)
+    note(f"  max err {err:.3e}")
+    assert err <= DECODE_TOL
+    assert np.all(got[3] == 0)
+
+
+@pytest.mark.parametrize("P", [17, 255, 4096])
+def test_wide_head_widths(P):
+    # one head split over P CTAs, from just above the in-kernel merge width to the maximum
+    q, k, v, sl = inputs(1, 8, 1, 128, [65536], seed=91)
+    T = 16
+    assert ctas_per_head(sl, 1, T, P).max() == P
+    err, _ = decode_err(q, k, v, sl, tile_keys=T, num_ctas=P)
+    note(f"decode one head over P={P}: max err {err:.3e}")
+    assert err <= DECODE_TOL
+    # a second call reuses the workspace: same values up to the fp32 summation order that
+    # the waves' dynamic block claims choose
+    again = gpu_decode(q, k, v, sl, tile_keys=T, num_ctas=P)
+    assert np.abs(again - gpu_decode(q, k, v, sl, tile_keys=T, num_ctas=P)).max() <= 1e-5

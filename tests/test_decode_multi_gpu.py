@@ -96,3 +96,13 @@ def test_multi_token_full_size_llama3():
     assert err <= DECODE_TOL
     del q, k, v
     torch.cuda.empty_cache()
+
+
+def test_multi_token_wide_head_with_masked_partials():
+    # G = 1, gamma = 16, 16-key tiles over 300 CTAs: each head is merged by the wide merge
+    # kernel, and the partials of the last keys hold no key that the first drafted tokens
+    # may see (their running max is -inf)
+    q, k, v, sl = multi_inputs(1, 2, 2, 128, 16, [3000], seed=84)
+    err, _ = multi_err(q, k, v, sl, tile_keys=16, num_ctas=300)
+    note(f"multi-token wide head: max err {err:.3e}")
+    assert err <= DECODE_TOL

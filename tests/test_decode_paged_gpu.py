@@ -86,3 +86,20 @@ def test_paged_full_size_llama3():
     assert err <= DECODE_TOL
     del q, k, v, kp, vp
     torch.cuda.empty_cache()
+
+
+def test_paged_wide_head():
+    # 16-key blocks, one long head split over 200 CTAs (wide merge kernel)
+    sl = [30000, 100]
+    shape = W.DecodeShape("p", 2, 8, 1, 128, tuple(sl), seed=62)
+    q, k, v, _ = W.decode_inputs(shape, device="cuda")
+    kp, vp, table = to_paged(k, v, sl, 16, seed=62)
+    got = A.attn_decode_paged(q, kp, vp, table, sl, tile_keys=64, num_ctas=200)
+    torch.cuda.synchronize()
+    got = got.cpu().double().numpy()
+    base = gpu_decode(q, k, v, sl, tile_keys=64, num_ctas=200)
+    assert np.abs(got - base).max() <= 1e-5
+    ref = oracle_decode(q, k, v, sl, 1, 1 / math.sqrt(128))
+    err = float(np.abs(got - ref).max())
+    note(f"paged wide head: max err {err:.3e}")
+    assert err <= DECODE_TOL

@@ -27,9 +27,9 @@ def harness(tmp_path_factory):
     lib.harness_pieces.restype = ctypes.c_int64
     lib.harness_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
-    lib.harness_merge_tree.restype = ctypes.c_int
-    lib.harness_merge_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+    lib.harness_segment_ctas.restype = ctypes.c_int
+    lib.harness_segment_ctas.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.harness_muldiv.restype = ctypes.c_int64
     lib.harness_muldiv.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.harness_cta_begin.restype = ctypes.c_int64
@@ -174,36 +174,66 @@ def test_library_planner_matches_header(harness):
         assert mine[0, 3] == cta[c] and mine[-1, 4] == cta[c + 1]
 
 
-# ------------------------------------------------------------- fused merge tree
+# ------------------------------------------------------- split heads and wide merge
 
-MERGE_FAN_IN, MERGE_LEVELS, MAX_CTAS = 16, 3, 4096  # the kernel's tree shape
-
-
-def merge_tree(harness, k, order):
-    order = np.ascontiguousarray(order, dtype=np.int32)
-    cov = np.zeros(k, dtype=np.int32)
-    left = ctypes.c_int64()
-    roots = harness.harness_merge_tree(k, MERGE_FAN_IN, MERGE_LEVELS, order.ctypes.data, cov.ctypes.data,
-                                       ctypes.byref(left))
-    return roots, cov, left.value
+MERGE_FAN_IN, MAX_CTAS = 16, 4096   # heads split over more CTAs go to the wide merge kernel
+MAX_WIDE_HEADS = (MAX_CTAS + MERGE_FAN_IN - 2) // (MERGE_FAN_IN - 1)
 
 
-@pytest.mark.parametrize("k", [2, 3, 15, 16, 17, 31, 255, 256, 257, 1000, 4095, 4096])
-def test_merge_tree_covers_every_partial_once(harness, k):
-    """Whatever order the CTAs of a split head finish in, exactly one of them produces the
-    output, it folds in every partial exactly once, and every counter is back at zero."""
-    rng = np.random.default_rng(k)
-    for trial in range(3):
-        order = np.arange(k) if trial == 0 else (np.arange(k)[::-1] if trial == 1 else rng.permutation(k))
-        roots, cov, left = merge_tree(harness, k, order)
-        assert roots == 1
-        assert np.all(cov == 1)
-        assert left == 0
+def segment_ctas(harness, sl, KH, T, P, splits=0):
+    sl = np.ascontiguousarray(sl, dtype=np.int32)
+    c_lo = np.zeros(len(sl) * KH, dtype=np.int32)
+    n = np.zeros(len(sl) * KH, dtype=np.int32)
+    wide = harness.harness_segment_ctas(sl.ctypes.data, len(sl), KH, T, P, splits, MERGE_FAN_IN, c_lo.ctypes.data,
+                                        n.ctypes.data)
+    return c_lo, n, wide
 
 
-def test_merge_tree_depth_bound():
-    # kMaxCtas partials of one head need exactly kMergeLevels levels of fan-in 16
-    assert MERGE_FAN_IN ** MERGE_LEVELS == MAX_CTAS
+@pytest.mark.parametrize("sl,KH,T,P,splits", [
+    ([262144], 1, 256, 256, 0),                # one long head over every CTA
+    ([5000, 0, 17, 70000, 3], 3, 64, 97, 0),
+    ([8192] * 16, 8, 256, 256, 0),
+    ([100, 2000, 40000], 2, 16, 1000, 0),
+    ([4000, 33, 0, 9000], 2, 64, 0, 20),      # fixed split with more than 16 chunks per head
+])
+def test_segment_ctas_match_the_pieces(harness, sl, KH, T, P, splits):
+    """The CTAs that plan_segment_ctas names for a head are exactly those that hold one of its
+    pieces, and the heads split over more than 16 CTAs are counted as wide."""
+    c_lo, n, wide = segment_ctas(harness, sl, KH, T, P, splits)
+    rows = pieces(harness, sl, KH, T, P, splits)
+    for s in range(len(sl) * KH):
+        b, kh = divmod(s, KH)
+        owners = sorted(set(rows[(rows[:, 1] == b) & (rows[:, 2] == kh)][:, 0].tolist()))
+        if not owners:
+            assert n[s] == 0
+            continue
+        assert owners == list(range(owners[0], owners[0] + len(owners)))
+        assert (c_lo[s], n[s]) == (owners[0], len(owners))
+    assert wide == int((n > MERGE_FAN_IN).sum())
+
+
+def test_wide_heads_stay_within_the_kernel_argument_list(harness):
+    """A head split over more than 16 CTAs owns the whole ranges of at least 15 of them, so a
+    plan of at most 4096 CTAs has at most ceil(4096 / 15) such heads (the merge kernel's
+    list).  Checked on the densest packing: heads just long enough to span 17 CTAs."""
+    rng = np.random.default_rng(3)
+    worst = 0
+    for per_cta in [1, 2, 3, 4]:
+        for extra in [1, per_cta, 2 * per_cta - 1]:
+            L = 15 * per_cta + extra          # tiles of T = 1 key per head
+            KH = 2
+            B = min(256, MAX_CTAS * per_cta // (KH * L) + 1)
+            _, n, wide = segment_ctas(harness, [L] * B, KH, 1, MAX_CTAS, 0)
+            worst = max(worst, wide)
+            assert wide <= MAX_WIDE_HEADS
+    for _ in range(20):
+        B = int(rng.integers(1, 257))
+        sl = rng.integers(0, 4000, size=B)
+        KH = int(rng.integers(1, 9))
+        P = int(min(MAX_CTAS, max(1, KH * sl.sum())))
+        _, _, wide = segment_ctas(harness, sl, KH, 1, P, 0)
+        assert wide <= MAX_WIDE_HEADS
+    assert worst > 200  # the packing above really comes close to the bound
 
 
 # ------------------------------------------------- exact integer arithmetic limits
