@@ -31,9 +31,11 @@
 //      ~2^-17 relative accuracy instead of bf16's 2^-9.
 //  The key order inside each MFMA contraction is chosen so that the lanes that
 //  hold S^T after step 2 already hold the P^T operand of step 5, and step 4
-//  reads V^T in that same key order: no shuffles beyond the two row-max steps.  At the end of a piece the wave states are merged through
-//  LDS (max, rescale, tree sum) and written either as the final output or,
-//  when the head is split over several CTAs, as a partial slot.  A head split
+//  reads V^T in that same key order: no shuffles beyond the two row-max steps.
+//  At the end of a piece every wave parks its state in LDS and, after one
+//  barrier, each thread merges one float4 column over the waves (max,
+//  rescale, sum) and writes it either as the final output or, when the head
+//  is split over several CTAs, into a partial slot.  A head split
 //  over at most 16 CTAs is merged by the CTA that arrives last at its atomic
 //  counter, which rescales the partials to their common max.  A wider head is
 //  merged by merge_wide_kernel, launched next on the stream: one CU reads only
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     uint16_t *stages = reinterpret_cast<uint16_t *>(smem);
     float *sm_m = smem;               // [W][16]
     float *sm_l = smem + W * 16;      // [W][16]
-    float *sm_o = smem + 2 * W * 16;  // [W/2][G][OSTRIDE]
+    float *sm_o = smem + 2 * W * 16;  // [W][NC][OSTRIDE]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: block indices stay scalar
@@ -612,6 +614,10 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         }
 
         // ---- merge the W wave states of this piece ----
+        // Every wave parks its (m, l, O) in LDS; after one barrier each thread
+        // merges one float4 column of the piece's NC x HSZ state over the W
+        // waves (rescale to the common max, sum) and stores it straight to the
+        // output or to the partial slot.
         l_run = wave_sum_over_groups(l_run);
         __syncthreads();  // every wave left the streaming loop: stages and block counter are free
         if (threadIdx.x == 0) blk_next = W;  // for the next piece (later barriers publish it)
@@ -619,56 +625,50 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             sm_m[wave * 16 + col] = m_run;
             sm_l[wave * 16 + col] = l_run;
         }
+        if (col < NC) {
+            float *dst = sm_o + (wave * NC + col) * OSTRIDE + 4 * grp;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db];
+        }
         __syncthreads();
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + col]);
-        float Lt = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const float mw = sm_m[w * 16 + col];
-            Lt += mw == NEG_INF ? 0.f : sm_l[w * 16 + col] * __builtin_amdgcn_exp2f(mw - M);
-        }
-        const float f = m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db] *= f;
-#pragma unroll
-        for (int half = W / 2; half >= 1; half >>= 1) {
-            if (wave >= half && wave < 2 * half && col < NC) {
-                float *dst = sm_o + ((wave - half) * NC + col) * OSTRIDE + 4 * grp;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db];
-            }
-            __syncthreads();
-            if (wave < half && col < NC) {
-                const float *src = sm_o + (wave * NC + col) * OSTRIDE + 4 * grp;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) oacc[db] += *reinterpret_cast<const f32x4 *>(src + 16 * db);
-            }
-            __syncthreads();
-        }
 
         const bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
-        if (wave == 0 && col < NC) {
+        const int64_t so = whole ? 0 : (int64_t)plan_slot(pl, c, pc.seg_begin) * p.slot_floats;
+        constexpr int UNITS = (kMaxGroup * HSZ / 4 + W * 64 - 1) / (W * 64);  // float4 columns per thread, at most
+        const int units = NC * HSZ / 4;
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r) {
+            const int u = threadIdx.x + r * W * 64;
+            if (u >= units) continue;
+            const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
+            float M = NEG_INF;
+#pragma unroll
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
+            float Lt = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float mw = sm_m[w * 16 + g];
+                const float f = mw == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                Lt += sm_l[w * 16 + g] * f;
+                O += *reinterpret_cast<const f32x4 *>(sm_o + (w * NC + g) * OSTRIDE + 4 * d4) * f;
+            }
             if (whole) {
-                const float inv = p.v_scale / Lt;
-                float *dst = p.out + (((int64_t)pc.b * p.Hq + h0 + col % G) * p.qlen + col / G) * HSZ + 4 * grp;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db] * inv;
+                // column g: token g / G, head g % G
+                float *dst = p.out + (((int64_t)pc.b * p.Hq + h0 + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
+                *reinterpret_cast<f32x4 *>(dst) = O * (p.v_scale / Lt);
             } else {
-                float *slot = p.ws + (int64_t)plan_slot(pl, c, pc.seg_begin) * p.slot_floats;
-                float *dst = slot + col * HSZ + 4 * grp;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) st_shared_f4(dst + 16 * db, oacc[db]);
-                if (grp == 0) {
-                    st_shared_f(slot + NC * HSZ + col, M);
-                    st_shared_f(slot + NC * HSZ + NC + col, Lt);
+                st_shared_f4(p.ws + so + g * HSZ + 4 * d4, O);
+                if (d4 == 0) {
+                    st_shared_f(p.ws + so + NC * HSZ + g, M);
+                    st_shared_f(p.ws + so + NC * HSZ + NC + g, Lt);
                 }
             }
-            if (!whole) wait_memory();
         }
+        if (!whole) wait_memory();
         if (!whole) merge_up<HSZ, W * 64>(p, pl, pc, &merge_flag);
         t = pc.tile_end;
+        if (t < t_end) __syncthreads();  // the reduction buffers are read before the next piece's stages reuse them
     }
 }
 
@@ -676,7 +676,7 @@ template <int HSZ>
 size_t decode_tiles_lds_bytes(int G) {
     using C = DecodeCfg<HSZ>;
     const size_t stage = (size_t)C::W * C::STAGE * sizeof(uint16_t);
-    const size_t reduce = (size_t)(2 * C::W * 16 + (C::W / 2) * G * (HSZ + 4)) * sizeof(float);
+    const size_t reduce = (size_t)(2 * C::W * 16 + C::W * G * (HSZ + 4)) * sizeof(float);
     return stage > reduce ? stage : reduce;
 }
 
