@@ -24,6 +24,7 @@ ATTN_MAX_BATCH = 256
 ATTN_MAX_GROUP = 16
 ATTN_MAX_CTAS = 4096
 ATTN_DECODE_COUNTER_BYTES = 32768
+ATTN_DECODE_PLAN_BYTES = 8192
 ATTN_SCHEDULE_AUTO = 0
 ATTN_SCHEDULE_STREAM_K = 1
 ATTN_SCHEDULE_FIXED_SPLIT = 2
@@ -52,7 +53,7 @@ class attn_decode_args(ctypes.Structure):
         ("schedule", _I), ("num_splits", _I),
         ("kv_dtype", _I), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("block_table", _P), ("block_size", _I), ("max_blocks_per_seq", _I), ("num_blocks", _I),
-        ("q_len", _I),
+        ("q_len", _I), ("seqlens_on_device", _I),
     ]
 
 
@@ -135,6 +136,20 @@ def _host_seqlens(seqlens):
     return arr
 
 
+def _seqlens_arg(seqlens, B):
+    """(pointer, on_device, owner) for attn_decode_args.seqlens: a CUDA int32 tensor is
+    passed as device seqlens (never read on the host); anything else becomes a host array."""
+    import torch
+    if isinstance(seqlens, torch.Tensor) and seqlens.is_cuda:
+        if seqlens.dtype != torch.int32 or not seqlens.is_contiguous() or seqlens.numel() != B:
+            raise TypeError("device seqlens must be a contiguous int32 CUDA tensor with B entries")
+        return seqlens.data_ptr(), 1, seqlens
+    sl = _host_seqlens(seqlens)
+    if len(sl) != B:
+        raise ValueError("seqlens must have B entries")
+    return sl.ctypes.data, 0, sl
+
+
 def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
     """Decode step (``attn_decode``): q [B][Hq][Hsz], caches [B][KH][S][Hsz] bf16, S = max seqlens.
 
@@ -164,6 +179,9 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
                    num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
     """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
 
+    ``seqlens`` may be host values or a CUDA int32 tensor; the latter is passed as device
+    seqlens (the plan is then built on the device and the call can be graph-captured).
+
     ``workspace`` is an optional CUDA tensor used as the partial-state buffer; its first
     ``ATTN_DECODE_COUNTER_BYTES`` bytes must be zero before its first use (allocate it with
     ``torch.zeros``), and each call leaves them zero.  ``ev_tiles_begin/end`` are optional
@@ -176,16 +194,14 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
         raise TypeError("k_cache and v_cache must have the same element type")
     B, Hq, Hsz = q.shape
     KH, S = k_cache.shape[1], k_cache.shape[2]
-    sl = _host_seqlens(seqlens)
-    if len(sl) != B:
-        raise ValueError("seqlens must have B entries")
+    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
     if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
     if out is None:
         out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
     a = attn_decode_args()
     a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
     a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
     a.kv_stride = S
     a.scale = float(scale)
@@ -217,9 +233,7 @@ class PreparedDecode:
             raise TypeError("k_cache and v_cache must have the same element type")
         B, Hq, Hsz = q.shape
         KH, S = k_cache.shape[1], k_cache.shape[2]
-        self._sl = _host_seqlens(seqlens)
-        if len(self._sl) != B:
-            raise ValueError("seqlens must have B entries")
+        sl_ptr, on_dev, self._sl = _seqlens_arg(seqlens, B)
         if v_cache.shape != k_cache.shape or k_cache.shape[3] != Hsz:
             raise ValueError("k_cache/v_cache must share one shape ending in Hsz")
         if block_table is None and k_cache.shape[0] != B:
@@ -228,7 +242,7 @@ class PreparedDecode:
             raise ValueError("out must be a contiguous fp32 CUDA tensor [B][Hq][Hsz]")
         a = attn_decode_args()
         a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-        a.seqlens, a.out = self._sl.ctypes.data, out.data_ptr()
+        a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
         a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
         a.kv_stride = 0 if block_table is not None else S
         a.scale = float(scale)
@@ -326,14 +340,12 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seqlens, out=None, *, scal
     nblocks, KH, bs, Hsz2 = k_pool.shape
     if Hsz2 != Hsz or block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("pools must be [num_blocks][KH][block_size][Hsz], block_table [B][max_blocks]")
-    sl = _host_seqlens(seqlens)
-    if len(sl) != B:
-        raise ValueError("seqlens must have B entries")
+    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
     if out is None:
         out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
     a = attn_decode_args()
     a.q, a.k_cache, a.v_cache = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
-    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
     a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
     a.kv_stride = 0
     a.scale = float(scale)
@@ -362,16 +374,14 @@ def attn_decode_multi(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile
         raise TypeError("k_cache and v_cache must have the same element type")
     B, Hq, gamma, Hsz = q.shape
     KH, S = k_cache.shape[1], k_cache.shape[2]
-    sl = _host_seqlens(seqlens)
-    if len(sl) != B:
-        raise ValueError("seqlens must have B entries")
+    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
     if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
     if out is None:
         out = torch.empty((B, Hq, gamma, Hsz), dtype=torch.float32, device=q.device)
     a = attn_decode_args()
     a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-    a.seqlens, a.out = sl.ctypes.data, out.data_ptr()
+    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
     a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
     a.kv_stride = S
     a.scale = float(scale)

@@ -17,6 +17,7 @@
 static_assert(ATTN_MAX_GROUP == attn::kMaxGroup, "group limit mismatch");
 static_assert(ATTN_MAX_CTAS == attn::kMaxCtas, "CTA limit mismatch");
 static_assert(ATTN_DECODE_COUNTER_BYTES == attn::kCounterBytes, "counter region mismatch");
+static_assert(ATTN_DECODE_PLAN_BYTES == attn::kPlanAreaBytes, "plan area mismatch");
 
 namespace {
 
@@ -221,9 +222,16 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     const int qlen = a->q_len > 1 ? a->q_len : 1;
     if ((a->Hq / a->KH) * qlen > attn::kMaxGroup)
         return fail(ATTN_ERR_UNSUPPORTED, "G*q_len=%d exceeds %d query columns", (a->Hq / a->KH) * qlen, attn::kMaxGroup);
-    for (int b = 0; b < a->B; ++b)
-        if (a->seqlens[b] != 0 && a->seqlens[b] < qlen)
-            return fail(ATTN_ERR_SHAPE, "seqlens[%d]=%d holds fewer keys than q_len=%d", b, a->seqlens[b], qlen);
+    const bool dev_sl = a->seqlens_on_device != 0;
+    if (dev_sl) {
+        if (((uintptr_t)a->seqlens & 3u) != 0) return fail(ATTN_ERR_ALIGN, "device seqlens must be 4-byte aligned");
+        if (!a->block_table && a->kv_stride == 0)
+            return fail(ATTN_ERR_SHAPE, "device seqlens need an explicit kv_stride (or a block table)");
+    } else {
+        for (int b = 0; b < a->B; ++b)
+            if (a->seqlens[b] != 0 && a->seqlens[b] < qlen)
+                return fail(ATTN_ERR_SHAPE, "seqlens[%d]=%d holds fewer keys than q_len=%d", b, a->seqlens[b], qlen);
+    }
     if (a->schedule < ATTN_SCHEDULE_AUTO || a->schedule > ATTN_SCHEDULE_FIXED_SPLIT)
         return fail(ATTN_ERR_SHAPE, "schedule=%d is not an ATTN_SCHEDULE_* value", a->schedule);
     if (a->num_splits < 0) return fail(ATTN_ERR_SHAPE, "num_splits=%d is negative", a->num_splits);
@@ -265,8 +273,25 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     const int T = a->tile_keys > 0 ? a->tile_keys : attn::decode_tile_keys(a->Hsz);
 
     attn::DecodeParams p;
-    st = build_plan(a->seqlens, a->B, a->KH, T, stride, &p.plan);
-    if (st != ATTN_OK) return st;
+    if (dev_sl) {
+        // only the shape is known here; the device fills in L_b, the prefix and N
+        const int64_t nmax = (stride + T - 1) / T;  // tiles of the longest possible context
+        if ((int64_t)a->B * a->KH * nmax > 0x7fffffffLL)
+            return fail(ATTN_ERR_UNSUPPORTED, "B*KH*ceil(kv_stride/T)=%lld LeanTiles exceed 2^31; raise tile_keys",
+                        (long long)a->B * a->KH * nmax);
+        p.plan = LeanPlan{};
+        p.plan.B = a->B;
+        p.plan.KH = a->KH;
+        p.plan.T = T;
+        for (int b = 0; b <= a->B; ++b) p.plan.tile_prefix[b] = (int32_t)((int64_t)b * a->KH * nmax);  // upper bounds
+        p.plan.N = (int64_t)a->B * a->KH * nmax;
+        p.plan.mode = kPlanStreamK;
+        p.plan.splits = 1;
+    } else {
+        st = build_plan(a->seqlens, a->B, a->KH, T, stride, &p.plan);
+        if (st != ATTN_OK) return st;
+    }
+    p.plan_dev = nullptr;
     p.q = static_cast<const uint16_t *>(a->q);
     p.k = static_cast<const uint16_t *>(a->k_cache);
     p.v = static_cast<const uint16_t *>(a->v_cache);
@@ -314,15 +339,18 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         P = a->B * a->KH * S;
     } else {
         if (P == 0) P = resident < attn::kMaxCtas ? resident : attn::kMaxCtas;
-        if (P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;  // no empty CTA; one CTA zeroes an all-empty batch
+        // no empty CTA; one CTA zeroes an all-empty batch (with device seqlens the device clamps P)
+        if (!dev_sl && P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;
     }
     p.plan.P = P;
     p.counters = nullptr;
 
     attn::WideMergeParams wide;
     wide.count = 0;
-    bool split = false;
-    if (p.plan.N > 0 && !scan_segments(p.plan, &split, &wide))
+    wide.count_dev = nullptr;
+    wide.head_dev = nullptr;
+    bool split = dev_sl;  // with device seqlens the host cannot tell: always bring the workspace
+    if (!dev_sl && p.plan.N > 0 && !scan_segments(p.plan, &split, &wide))
         return fail(ATTN_ERR_UNSUPPORTED, "more than %d heads split over more than %d workgroups", attn::kMaxWideHeads,
                     attn::kMergeFanIn);
     if (split) {
@@ -339,10 +367,30 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
             w = static_cast<char *>(lw);
         }
         p.counters = reinterpret_cast<int *>(w);
-        p.ws = reinterpret_cast<float *>(w + attn::kCounterBytes);
+        p.ws = reinterpret_cast<float *>(w + attn::kCounterBytes + attn::kPlanAreaBytes);
+        if (dev_sl) {
+            char *area = w + attn::kCounterBytes;
+            p.plan_dev = reinterpret_cast<const LeanPlan *>(area);
+            wide.count_dev = reinterpret_cast<const int *>(area + attn::kWideCountOffset);
+            wide.head_dev = reinterpret_cast<const attn::WideHead *>(area + attn::kWideListOffset);
+        }
     }
 
     hipError_t e;
+    if (dev_sl) {
+        const attn::PlanBase base = {a->B, a->KH, T, p.plan.mode, p.plan.splits, P};
+        char *area = reinterpret_cast<char *>(const_cast<LeanPlan *>(p.plan_dev));
+        e = attn::launch_plan_device(a->seqlens, base, stride, reinterpret_cast<LeanPlan *>(area),
+                                     reinterpret_cast<int *>(area + attn::kWideCountOffset),
+                                     reinterpret_cast<attn::WideHead *>(area + attn::kWideListOffset), stream);
+        if (e != hipSuccess) return fail_hip(e, "device plan kernel launch");
+        // the most heads that can be split over more than kMergeFanIn CTAs
+        const int64_t segs = (int64_t)a->B * a->KH;
+        int64_t most = p.plan.mode == kPlanFixedSplit ? (p.plan.splits > attn::kMergeFanIn ? segs : 0)
+                                                      : P / (attn::kMergeFanIn - 1);
+        most = most < segs ? most : segs;
+        wide.count = (int)(most < attn::kMaxWideHeads ? most : attn::kMaxWideHeads);
+    }
     if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
         return fail_hip(e, "hipEventRecord(begin)");
     e = attn::launch_decode_tiles(p, a->Hsz, fp8, stream);

@@ -37,6 +37,7 @@ struct DecodeParams {
     int max_blocks_per_seq;
     int log2_block_size;
     int num_blocks;
+    const LeanPlan *plan_dev;  // non-NULL: the plan was built on the device (seqlens in device memory)
     LeanPlan plan;
 };
 
@@ -59,6 +60,8 @@ struct WideHead {
 };
 
 struct WideMergeParams {
+    const int *count_dev;          // non-NULL: the list was built on the device, head_dev[0 .. *count_dev)
+    const WideHead *head_dev;
     const float *ws;      // partial slots
     float *out;           // fp32 [B][Hq][qlen][Hsz]
     int slot_floats;
@@ -69,15 +72,30 @@ struct WideMergeParams {
 };
 
 // Workspace layout: int counters[2 * kMaxCtas] (a fixed-size region, so its
-// place never depends on P), then float slots[2P][slot_floats].
+// place never depends on P), then a plan area that a call with device seqlens
+// fills on the device (the LeanPlan, then the wide-head count and list), then
+// float slots[2P][slot_floats].
 constexpr size_t kCounterBytes = (size_t)2 * kMaxCtas * sizeof(int);
+constexpr size_t kPlanAreaBytes = 8192;
+constexpr size_t kWideCountOffset = 4096;  // within the plan area
+constexpr size_t kWideListOffset = 4112;
+static_assert(sizeof(LeanPlan) <= kWideCountOffset, "plan area too small for the plan");
+static_assert(kWideListOffset + kMaxWideHeads * sizeof(WideHead) <= kPlanAreaBytes, "plan area too small for the list");
 inline size_t decode_workspace_bytes(int P, int NC, int Hsz) {
-    return kCounterBytes + (size_t)2 * P * decode_slot_floats(NC, Hsz) * sizeof(float);
+    return kCounterBytes + kPlanAreaBytes + (size_t)2 * P * decode_slot_floats(NC, Hsz) * sizeof(float);
 }
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream);
 hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream);
+// Builds the LeanPlan of `base` (B, KH, T, mode, splits, P) for the device
+// seqlens on the device, clamping each L_b into [0, stride], and lists the wide
+// heads; one workgroup.
+struct PlanBase {
+    int B, KH, T, mode, splits, P;  // P: launched CTAs (stream-K) or B*KH*splits (fixed split)
+};
+hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int64_t stride, LeanPlan *plan_out,
+                              int *wide_count, WideHead *wide, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int NC);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave

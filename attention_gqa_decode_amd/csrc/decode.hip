@@ -45,8 +45,12 @@
 //  ever waits for another, so neither merge needs co-residency.
 #include "common.h"
 
+#include <atomic>
+
 namespace attn {
 namespace {
+
+constexpr int kMaxDevices = 64;
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -388,7 +392,13 @@ __device__ __forceinline__ void combine_state(float &M, float &L, f32x4 &O, floa
 // spread over many CUs instead of read by the one CTA that arrives last.
 template <int HSZ>
 __global__ __launch_bounds__(256) void merge_wide_kernel(const WideMergeParams mp) {
-    const WideHead hd = mp.head[blockIdx.y];
+    WideHead hd;
+    if (mp.count_dev) {  // list built on the device: the grid covers the most heads there can be
+        if ((int)blockIdx.y >= *mp.count_dev) return;
+        hd = mp.head_dev[blockIdx.y];
+    } else {
+        hd = mp.head[blockIdx.y];
+    }
     const int b = hd.bkh & 255, kh = hd.bkh >> 8;
     const int c_lo = hd.cta & 4095, n = ((hd.cta >> 12) & 4095) + 1;
     const int slot0 = 2 * c_lo + (hd.cta >> 24);
@@ -451,6 +461,71 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const WideMergeParams m
         float *dst = mp.out + (((int64_t)b * mp.Hq + kh * G + g % G) * mp.qlen + g / G) * HSZ + col;
         *reinterpret_cast<f32x4 *>(dst) = O * (mp.v_scale / L);
     }
+}
+
+// The LeanPlan of a call whose seqlens live in device memory, built on the
+// device so that the call needs no host read of them (and can be captured in a
+// graph): L_b clamped into [0, stride], the tile prefix (one scan over the
+// batch), N, P = min(launched CTAs, N) for stream-K, and the heads split over
+// more than kMergeFanIn CTAs for merge_wide_kernel.  The same numbering as the
+// host planner (plan.h), so the tile kernel cannot tell the two apart.
+static_assert(ATTN_MAX_BATCH == 256, "plan_device_kernel maps one thread to each request slot");
+__global__ __launch_bounds__(256) void plan_device_kernel(const int32_t *seqlens, const PlanBase base, int64_t stride,
+                                                          LeanPlan *plan_out, int *wide_count, WideHead *wide) {
+    __shared__ LeanPlan lp;
+    __shared__ int64_t part[256];
+    __shared__ int nwide;
+    const int tid = threadIdx.x;
+    const int B = base.B, KH = base.KH;
+    int64_t tiles = 0;
+    int L = 0;
+    if (tid < B) {
+        L = seqlens[tid];
+        L = L < 0 ? 0 : (L > stride ? (int)stride : L);
+        tiles = (int64_t)KH * ((L + (int64_t)base.T - 1) / base.T);
+    }
+    lp.seqlen[tid] = L;
+    part[tid] = tiles;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the tiles per request
+        const int64_t v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    const int64_t N = part[255];
+    lp.tile_prefix[tid] = (int32_t)(tid < B ? part[tid] - tiles : N);
+    if (tid == 0) {
+        lp.tile_prefix[256] = (int32_t)N;
+        lp.B = B;
+        lp.KH = KH;
+        lp.T = base.T;
+        lp.N = N;
+        lp.mode = base.mode;
+        lp.splits = base.splits;
+        lp.P = base.mode == kPlanStreamK ? (int)(N < base.P ? (N > 0 ? N : 1) : base.P) : base.P;
+        nwide = 0;
+    }
+    __syncthreads();
+    for (int s = tid; s < B * KH; s += 256) {
+        const int b = s / KH, kh = s - b * KH;
+        const int nb = plan_tiles_per_segment(lp, b);
+        if (nb == 0) continue;
+        const int64_t s0 = lp.tile_prefix[b] + (int64_t)kh * nb;
+        const SegmentCtas sc = plan_segment_ctas(lp, s0, s0 + nb);
+        if (sc.n > kMergeFanIn) {
+            const int i = atomicAdd(&nwide, 1);  // at most kMaxWideHeads (see WideMergeParams)
+            if (i < kMaxWideHeads) {
+                wide[i].bkh = b | kh << 8;
+                wide[i].cta = sc.c_lo | (sc.n - 1) << 12 | (plan_slot(lp, sc.c_lo, s0) & 1) << 24;
+            }
+        }
+    }
+    const int *src = reinterpret_cast<const int *>(&lp);
+    int *dst = reinterpret_cast<int *>(plan_out);
+    for (int i = tid; i < (int)(sizeof(LeanPlan) / sizeof(int)); i += 256) dst[i] = src[i];
+    __syncthreads();
+    if (tid == 0) *wide_count = nwide < kMaxWideHeads ? nwide : kMaxWideHeads;
 }
 
 // K/V rows of the context of request b under kv head kh.
@@ -532,13 +607,20 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     __shared__ LeanPlan plan_lds;
     {
         constexpr int WORDS = (int)(sizeof(LeanPlan) / sizeof(int));
-        const int *src = reinterpret_cast<const int *>(&p.plan);
         int *dst = reinterpret_cast<int *>(&plan_lds);
-        for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
+        if (p.plan_dev) {  // built on the device from device seqlens
+            const int *src = reinterpret_cast<const int *>(p.plan_dev);
+            for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
+        } else {
+            const int *src = reinterpret_cast<const int *>(&p.plan);
+            for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
+        }
         if (threadIdx.x == 0) blk_next = W;
         __syncthreads();
     }
     const LeanPlan &pl = plan_lds;
+    // a plan built on the device uses min(P, N) of the launched CTAs
+    if (c >= __builtin_amdgcn_readfirstlane(pl.P)) return;
 
     // The first piece's first blocks are requested before any other set-up:
     // every wave's start-up instructions then run while they are in flight.
@@ -688,14 +770,30 @@ size_t tiles_lds_bytes(int Hsz, int G) {
     }
 }
 
+// Raises a kernel's dynamic-LDS limit (default 64 KiB; gfx950 has 160 KiB per
+// CU) to the largest size any call asks for, once per device and size, so
+// that launches captured into a graph make no attribute calls.
+hipError_t ensure_lds_limit(const void *fn, std::atomic<int> *done, size_t lds) {
+    if (lds <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::atomic<int> &d = done[dev < kMaxDevices ? dev : kMaxDevices - 1];
+    if (d.load(std::memory_order_acquire) >= (int)lds && dev < kMaxDevices) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int cur = d.load(std::memory_order_relaxed);
+    while (cur < (int)lds && !d.compare_exchange_weak(cur, (int)lds)) {
+    }
+    return hipSuccess;
+}
+
 template <int HSZ, bool FP8, bool PAGED>
 hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
     const size_t lds = decode_tiles_lds_bytes<HSZ>(p.NC);
-    if (lds > 65536) {  // above the default dynamic-LDS limit; gfx950 has 160 KiB per CU
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> lds_set[kMaxDevices];
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED>), lds_set, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8, PAGED>), dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds,
                        stream, p);
     return hipGetLastError();
@@ -753,6 +851,13 @@ hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t str
         case 256: return launch_merge_wide_h<256>(mp, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int64_t stride, LeanPlan *plan_out,
+                              int *wide_count, WideHead *wide, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_device_kernel, dim3(1), dim3(256), 0, stream, seqlens, base, stride, plan_out, wide_count,
+                       wide);
+    return hipGetLastError();
 }
 
 // Zero-fills `bytes` (a multiple of 4) with plain vector stores; used for the

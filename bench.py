@@ -91,9 +91,10 @@ def log(msg: str) -> None:
 
 
 def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0,
-                 fp8: bool = False, block_size: int = 0):
+                 fp8: bool = False, block_size: int = 0, device_seqlens: bool = False):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
-    events recorded on the launch stream around every decode-kernel launch (roofline)."""
+    events recorded on the launch stream around every decode-kernel launch (roofline).
+    With device_seqlens the lengths sit in a device tensor and the plan is built on the device."""
     import torch
 
     import attention_gqa_decode_amd as A
@@ -118,7 +119,8 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
                                   block_table=paged[i][2]) for i in range(copies)]
         torch.cuda.empty_cache()
     else:
-        calls = [A.PreparedDecode(q, ks[i], vs[i], sl, out, scale=scale, schedule=schedule) for i in range(copies)]
+        sl_arg = torch.tensor(sl, dtype=torch.int32, device="cuda") if device_seqlens else sl
+        calls = [A.PreparedDecode(q, ks[i], vs[i], sl_arg, out, scale=scale, schedule=schedule) for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         calls[i % copies](stream)
@@ -311,6 +313,7 @@ def main():
     log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, kernel {r['kernel_us']:.1f} us")
     others = []
     schedules = []
+    devseq = []
     multi = None
     probe = None
     prefill = None
@@ -342,6 +345,14 @@ def main():
                               "fixed_split_us": round(fs["us_per_step"], 2),
                               "fixed_split_over_stream_k": round(fs["us_per_step"] / sk["us_per_step"], 3)})
             log(f"  {name}: stream-K {sk['us_per_step']:.1f} us, fixed split {fs['us_per_step']:.1f} us")
+        log("device seqlens (plan built on the device) vs host seqlens ...")
+        for name in ["llama3_8b", "long_mqa"]:
+            shp = W.decode_workload(name)
+            hs = bench_decode(shp, args.steps, args.warmup, hev)
+            ds = bench_decode(shp, args.steps, args.warmup, hev, device_seqlens=True)
+            devseq.append({"workload": name, "host_seqlens_us": round(hs["us_per_step"], 2),
+                           "device_seqlens_us": round(ds["us_per_step"], 2)})
+            log(f"  {name}: host {hs['us_per_step']:.1f} us, device {ds['us_per_step']:.1f} us")
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
@@ -380,6 +391,7 @@ def main():
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],
         "schedules": schedules,
+        "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,
         "hbm_probes": probe,

@@ -65,6 +65,8 @@ enum attn_status {
 /* Bytes at the start of a decode workspace that hold the merge counters
  * (one arrival counter per partial slot). */
 #define ATTN_DECODE_COUNTER_BYTES 32768
+/* Bytes after the counters that hold a plan built on the device (device seqlens). */
+#define ATTN_DECODE_PLAN_BYTES 8192
 
 /*
  * attn_decode -- one decode step of GQA attention (query length 1).
@@ -137,7 +139,7 @@ typedef struct attn_decode_args {
     const void *q;            /* bf16 [B][Hq][Hsz] */
     const void *k_cache;      /* [B][KH][kv_stride][Hsz], element type kv_dtype */
     const void *v_cache;      /* same layout and type as k_cache */
-    const int32_t *seqlens;   /* HOST int32 [B], 0 <= L_b <= kv_stride */
+    const int32_t *seqlens;   /* HOST int32 [B], 0 <= L_b <= kv_stride (DEVICE with seqlens_on_device) */
     float *out;               /* fp32 [B][Hq][Hsz] */
     int B, Hq, KH, Hsz;
     int64_t kv_stride;        /* cache capacity S per (b, kv head); 0 = max_b L_b */
@@ -176,6 +178,17 @@ typedef struct attn_decode_args {
      * the last gamma of each context, and query t attends keys 0 .. L_b - gamma + t.
      * Needs G * gamma <= ATTN_MAX_GROUP and L_b = 0 or L_b >= gamma. */
     int q_len;                /* 0 or 1 = one query token per request */
+    /* Device seqlens.  Nonzero: `seqlens` is a DEVICE int32 [B] that the call never
+     * reads on the host.  A one-workgroup kernel builds the LeanTile plan on the
+     * device in front of the decode kernel, so the call needs no synchronisation
+     * and can be captured in a graph whose replays see new lengths.  kv_stride must
+     * then be given (> 0) unless a block table is; each L_b is clamped into
+     * [0, kv_stride] (or the table's capacity) on the device, and a nonzero L_b below
+     * q_len gives undefined rows for that request.  Such a call always needs the
+     * workspace, and with num_ctas = 0 it launches every resident workgroup (those
+     * beyond the tile count exit at once).  A caller-owned workspace makes the call
+     * allocation-free. */
+    int seqlens_on_device;
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
@@ -184,8 +197,9 @@ int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
  * Bytes of workspace attn_decode_ex needs for these sizes when it runs with
  * `num_ctas` workgroups (0 = the library's default for the current device;
  * that query initialises the HIP runtime): ATTN_DECODE_COUNTER_BYTES of merge
- * counters, then 2 partial slots per workgroup of (G*Hsz + 2G) floats rounded
- * up to 16 bytes.  Returns 0 for unsupported sizes.
+ * counters, ATTN_DECODE_PLAN_BYTES for a plan built on the device, then 2
+ * partial slots per workgroup of (G*Hsz + 2G) floats rounded up to 16 bytes.
+ * Returns 0 for unsupported sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas);
 

@@ -123,10 +123,18 @@ def ex_args(**kw):
     (dict(Hq=2, KH=2, q_len=5), A.ATTN_ERR_SHAPE),                 # 4 cached keys < 5 query tokens
     (dict(seqlens=(4, 70), block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8),
      A.ATTN_ERR_SHAPE),                                           # 70 keys > 4 blocks x 16
+    (dict(seqlens_on_device=1), A.ATTN_ERR_SHAPE),                # device seqlens need kv_stride
+    (dict(seqlens_on_device=1, kv_stride=1 << 30, tile_keys=1), A.ATTN_ERR_UNSUPPORTED),  # > 2^31 tiles
 ])
 def test_decode_ex_rejects_bad_arguments(kw, status):
     a, _sl = ex_args(**kw)
     assert A.lib().attn_decode_ex(ctypes.byref(a), None) == status
+
+
+def test_decode_ex_device_seqlens_alignment():
+    a, _sl = ex_args(seqlens_on_device=1, kv_stride=64)
+    a.seqlens = FAKE + 2  # a device address, never read on the host
+    assert A.lib().attn_decode_ex(ctypes.byref(a), None) == A.ATTN_ERR_ALIGN
 
 
 def test_decode_ex_null_args():
@@ -164,8 +172,8 @@ def test_plan_argument_checks():
 
 def test_workspace_bytes_formula():
     # the counter region, then 2 slots per CTA, each G*Hsz (O) + 2G (m, l) floats rounded up to 4
-    C = A.ATTN_DECODE_COUNTER_BYTES
-    assert C == 2 * A.ATTN_MAX_CTAS * 4  # one arrival counter per partial slot
+    assert A.ATTN_DECODE_COUNTER_BYTES == 2 * A.ATTN_MAX_CTAS * 4  # one arrival counter per partial slot
+    C = A.ATTN_DECODE_COUNTER_BYTES + A.ATTN_DECODE_PLAN_BYTES
     assert A.attn_decode_workspace_bytes(16, 32, 8, 128, 100) == C + 2 * 100 * ((4 * 128 + 8 + 3) & ~3) * 4
     assert A.attn_decode_workspace_bytes(1, 8, 1, 64, 7) == C + 2 * 7 * ((8 * 64 + 16 + 3) & ~3) * 4
     assert A.attn_decode_workspace_bytes(1, 8, 3, 64, 7) == 0  # Hq % KH != 0
