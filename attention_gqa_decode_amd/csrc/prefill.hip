@@ -209,32 +209,31 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int dt = 0; dt < PF_HSZ / 32; ++dt) oacc[dt] *= alpha;
             }
             m_run = m_new;
-            f16x8 pb[4];  // P^T operands of the four 16-key chunks
+            // ---- P and BMM2, one 16-key chunk at a time: O^T += V^T P^T, contraction
+            //      slot 8h + e of chunk c is key 16c + 4h + e (e < 4) or 16c + 8 + 4h +
+            //      (e - 4) (e >= 4).  The chunk's four MFMAs run while the next chunk's
+            //      exponentials issue. ----
             const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+            const int t = lane & 15;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
+                f16x8 pb;  // P^T operand of chunk c
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    pb[c][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + e], scale_log2, -m_new));
+                    pb[e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + e], scale_log2, -m_new));
                 // the running sum adds the fp16-rounded weights the product uses
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const f16x2 pair = {pb[c][e], pb[c][e + 1]};
+                    const f16x2 pair = {pb[e], pb[e + 1]};
                     l_run = __builtin_amdgcn_fdot2(pair, ones, l_run, false);
                 }
-            }
-            // ---- BMM2: O^T += V^T P^T; contraction slot 8h + e of chunk c is key
-            //      16c + 4h + e (e < 4) or 16c + 8 + 4h + (e - 4) (e >= 4) ----
-            const int t = lane & 15;
 #pragma unroll
-            for (int dt = 0; dt < PF_HSZ / 32; ++dt) {
-                const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int dt = 0; dt < PF_HSZ / 32; ++dt) {
+                    const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
                     const i16x4 lo = v_cols(vs, 16 * c + 4 * h, d0, t);
                     const i16x4 hi = v_cols(vs, 16 * c + 8 + 4 * h, d0, t);
                     const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[dt] = mfma_pv(a, pb[c], oacc[dt]);
+                    oacc[dt] = mfma_pv(a, pb, oacc[dt]);
                 }
             }
         }
