@@ -27,6 +27,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -145,6 +146,8 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
         hev.destroy(b)
     nbytes = acc.decode_bytes(sl, shape.B, shape.Hq, shape.KH, shape.Hsz, kv_bytes=1 if fp8 else 2)
     kern_ms = sum(kern) / len(kern)
+    ks_sorted = sorted(kern)
+    pct = lambda f: ks_sorted[min(len(ks_sorted) - 1, int(f * len(ks_sorted)))] * 1e3
     res = {
         "workload": shape.name + ("_fp8" if fp8 else "") + (f"_paged{block_size}" if block_size else ""),
         "kv_dtype": "fp8_e4m3" if fp8 else "bf16", "B": shape.B, "Hq": shape.Hq, "KH": shape.KH, "Hsz": shape.Hsz,
@@ -152,6 +155,7 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
         "kv_copies_rotated": copies, "bytes_per_step": nbytes,
         "us_per_step": step_ms * 1e3, "GBps": nbytes / (step_ms * 1e-3) / 1e9,
         "kernel_us": kern_ms * 1e3, "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9,
+        "kernel_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
     }
     res["frac_of_peak"] = res["GBps"] / PEAK_HBM_GBPS
     del q, ks, vs, out, calls
@@ -278,7 +282,44 @@ def cpu_baseline(shape, budget_s: float = 12.0):
     nbytes = acc.decode_bytes(sl.tolist(), shape.B, shape.Hq, shape.KH, shape.Hsz)
     return {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} full {shape.name} decode step(s) (all {shape.B * shape.Hq} heads), "
-                      f"{per:.3f} s per step, fp64 plain C + OpenMP"}
+                      f"{per:.3f} s per step, fp64 plain C + OpenMP",
+            "single_thread_GBps": cpu_single_thread(shape), "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread(shape, heads: int = 32):
+    """The same oracle on one thread (OMP_NUM_THREADS=1, a child process that never touches
+    the GPU) over the first `heads` query heads of the workload, scaled to GB/s."""
+    code = (
+        "import math, sys, time; sys.path.insert(0, %r)\n"
+        "import numpy as np, oracle\n"
+        "from attention_gqa_decode_amd import workloads as W\n"
+        "from attention_gqa_decode_amd.workloads import bits\n"
+        "s = W.decode_workload(%r)\n"
+        "q, k, v, sl = W.decode_inputs(s, device='cpu')\n"
+        "qb, kb, vb = bits(q), bits(k), bits(v)\n"
+        "rows = np.arange(%d)\n"
+        "t = time.perf_counter(); oracle.decode(qb, kb, vb, sl.numpy(), s.Hq, s.KH, 1 / math.sqrt(s.Hsz), rows=rows)\n"
+        "print(time.perf_counter() - t, oracle.num_threads())\n" % (ROOT, shape.name, heads))
+    env = dict(os.environ, OMP_NUM_THREADS="1", HIP_VISIBLE_DEVICES="")
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        sec, thr = r.stdout.split()[-2:]
+    except (subprocess.SubprocessError, ValueError):
+        return None
+    # K/V bytes the sampled heads read, plus their q and out rows
+    L = shape.seqlens
+    per_head = [2 * L[(h // shape.Hq)] * shape.Hsz * 2 // (shape.Hq // shape.KH) + shape.Hsz * 6 for h in range(heads)]
+    return round(sum(per_head) / float(sec) / 1e9, 4) if int(thr) == 1 else None
 
 
 def main():
