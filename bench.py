@@ -301,6 +301,7 @@ def cpu_single_thread(shape, heads: int = 32):
     the GPU) over the first `heads` query heads of the workload, scaled to GB/s."""
     code = (
         "import math, sys, time; sys.path.insert(0, %r)\n"
+        "import torch; torch.set_num_threads(1)  # torch's OpenMP runtime is the oracle's too\n"
         "import numpy as np, oracle\n"
         "from attention_gqa_decode_amd import workloads as W\n"
         "from attention_gqa_decode_amd.workloads import bits\n"
@@ -314,7 +315,9 @@ def cpu_single_thread(shape, heads: int = 32):
     try:
         r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
         sec, thr = r.stdout.split()[-2:]
-    except (subprocess.SubprocessError, ValueError):
+    except (subprocess.SubprocessError, ValueError) as e:
+        tail = getattr(e, "stderr", None) or (r.stderr if "r" in locals() else "")
+        log(f"  one-thread oracle sample failed: {type(e).__name__}: {str(tail)[-400:]}")
         return None
     # K/V bytes the sampled heads read, plus their q and out rows
     L = shape.seqlens
