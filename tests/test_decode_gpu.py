@@ -143,11 +143,12 @@ def test_one_workspace_across_cta_counts():
         assert np.abs(got - ref).max() <= DECODE_TOL, P
 
 
-@pytest.mark.parametrize("P", [17, 300, 4096])
-def test_deep_merge_trees(P):
-    # one head split over P CTAs: one, two and three levels of the fan-in-16 merge tree
+@pytest.mark.parametrize("P", [16, 17, 300, 4096])
+def test_one_head_over_many_ctas(P):
+    # one head split over P CTAs: at the in-kernel merge's width (16), just past it and far
+    # past it (the wide merge kernel)
     L = 16 * P + 5
-    note(f"decode merge tree: L={L}, T=16, P={P}")
+    note(f"decode one head over P={P}: L={L}, T=16")
     q, k, v, sl = inputs(1, 8, 1, 128, [L], seed=14 + P)
     err, got = decode_err(q, k, v, sl, tile_keys=16, num_ctas=P)
     note(f"  max err {err:.3e}")
