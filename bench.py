@@ -359,6 +359,7 @@ def main():
     schedules = []
     devseq = []
     multi = None
+    tiny = None
     probe = None
     prefill = None
     if not args.headline_only:
@@ -400,6 +401,11 @@ def main():
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
+        log("decode tiny (B=1, Hq=8, KH=2, L=1024: cache-resident, a latency figure only) ...")
+        t = bench_decode(W.decode_workload("tiny"), args.steps, args.warmup, hev, rotate=False)
+        tiny = {"workload": "tiny", "us_per_step": round(t["us_per_step"], 2), "kernel_us": round(t["kernel_us"], 2),
+                "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"]}
+        log(f"  {tiny['us_per_step']:.1f} us/step")
         probe = bench_copy_probe(max(3, args.steps // 5))
         log(f"copy probe {probe['copy_read_plus_write_GBps']:.0f} GB/s, read probe {probe['read_GBps']:.0f} GB/s")
     cpu = None
@@ -438,6 +444,7 @@ def main():
         "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,
+        "tiny_latency": tiny,
         "hbm_probes": probe,
     }
     print(json.dumps(line), flush=True)
