@@ -53,7 +53,7 @@ class attn_decode_args(ctypes.Structure):
         ("schedule", _I), ("num_splits", _I),
         ("kv_dtype", _I), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("block_table", _P), ("block_size", _I), ("max_blocks_per_seq", _I), ("num_blocks", _I),
-        ("q_len", _I), ("seqlens_on_device", _I),
+        ("q_len", _I), ("seqlens_on_device", _I), ("out_lse", _P),
     ]
 
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.attn_hbm_copy_probe.restype = _I
     L.attn_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
     L.attn_hbm_read_probe.restype = _I
+    L.attn_merge_shards.argtypes = [_P, _P, _I, _I64, _I, _P, _P, _P]
+    L.attn_merge_shards.restype = _I
     L.attn_device_info.argtypes = [_P, _P]
     L.attn_device_info.restype = _I
     L.attn_release.argtypes = []
@@ -176,7 +178,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
 
 def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
                    workspace=None, ev_tiles_begin=None, ev_tiles_end=None, schedule=ATTN_SCHEDULE_AUTO,
-                   num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
+                   num_splits=0, k_scale=0.0, v_scale=0.0, out_lse=None, stream=None):
     """Full-control decode (``attn_decode_ex``); the cache capacity is ``k_cache.shape[2]``.
 
     ``seqlens`` may be host values or a CUDA int32 tensor; the latter is passed as device
@@ -213,7 +215,30 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     a.ev_tiles_end = ev_tiles_end
     a.schedule, a.num_splits = int(schedule), int(num_splits)
     a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
+    if out_lse is not None:
+        if out_lse.dtype != torch.float32 or not out_lse.is_cuda or out_lse.numel() != B * Hq:
+            raise TypeError("out_lse must be an fp32 CUDA tensor with B*Hq entries")
+        a.out_lse = out_lse.data_ptr()
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
+    return out
+
+
+def attn_merge_shards(outs, lses, out=None, lse_out=None, stream=None):
+    """Merge (``attn_merge_shards``) of S decode outputs over disjoint key ranges of the same
+    rows: ``outs`` fp32 [S][rows...][Hsz], ``lses`` fp32 [S][rows...] (each shard's ``out_lse``).
+    Returns ``out`` fp32 [rows...][Hsz]; ``lse_out`` (optional) receives the merged lse."""
+    import torch
+    for n, t in (("outs", outs), ("lses", lses)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous fp32 CUDA tensor")
+    S, Hsz = outs.shape[0], outs.shape[-1]
+    rows = outs.numel() // (S * Hsz)
+    if lses.shape[0] != S or lses.numel() != S * rows:
+        raise ValueError("lses must be [S][rows] matching outs [S][rows][Hsz]")
+    if out is None:
+        out = torch.empty(outs.shape[1:], dtype=torch.float32, device=outs.device)
+    _check(lib().attn_merge_shards(outs.data_ptr(), lses.data_ptr(), S, rows, Hsz, out.data_ptr(),
+                                   None if lse_out is None else lse_out.data_ptr(), _stream_handle(stream)))
     return out
 
 
@@ -226,7 +251,8 @@ class PreparedDecode:
     """
 
     def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
-                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, block_table=None):
+                 schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, block_table=None,
+                 out_lse=None):
         _bf16_cuda("q", q)
         kv_dtype = _kv_cuda("k_cache", k_cache)
         if _kv_cuda("v_cache", v_cache) != kv_dtype:
@@ -253,6 +279,9 @@ class PreparedDecode:
             a.block_table = block_table.data_ptr()
             a.block_size, a.max_blocks_per_seq, a.num_blocks = S, block_table.shape[1], k_cache.shape[0]
             self._table = block_table
+        if out_lse is not None:  # fp32 [B][Hq] on the device
+            a.out_lse = out_lse.data_ptr()
+            self._lse = out_lse
         self._args = a
         self._ref = ctypes.byref(a)
         self._fn = lib().attn_decode_ex

@@ -249,6 +249,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
                     attn::kMaxCtas);
     if (!(a->scale == a->scale) || isinf(a->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
     if (a->workspace && !aligned16(a->workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (((uintptr_t)a->out_lse & 3u) != 0) return fail(ATTN_ERR_ALIGN, "out_lse must be 4-byte aligned");
 
     int log2_bs = 0;
     if (a->block_table) {
@@ -296,6 +297,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.k = static_cast<const uint16_t *>(a->k_cache);
     p.v = static_cast<const uint16_t *>(a->v_cache);
     p.out = a->out;
+    p.lse = a->out_lse;
     p.ws = nullptr;
     p.kv_stride = stride;
     p.Hq = a->Hq;
@@ -400,6 +402,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (p.ws && wide.count > 0) {
         wide.ws = p.ws;
         wide.out = p.out;
+        wide.lse = p.lse;
         wide.slot_floats = p.slot_floats;
         wide.NC = p.NC;
         wide.G = p.G;
@@ -409,6 +412,20 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         e = attn::launch_merge_wide(wide, a->Hsz, stream);
         if (e != hipSuccess) return fail_hip(e, "wide merge kernel launch");
     }
+    return ATTN_OK;
+}
+
+int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out, float *lse_out,
+                      hipStream_t stream) {
+    g_last_error.clear();
+    if (!outs || !lses || !out) return fail(ATTN_ERR_NULL, "outs, lses and out must be non-NULL");
+    if (S <= 0 || rows < 0) return fail(ATTN_ERR_SHAPE, "S=%d must be positive and rows=%lld non-negative", S, (long long)rows);
+    if (Hsz <= 0 || Hsz % 4 != 0) return fail(ATTN_ERR_SHAPE, "Hsz=%d must be a positive multiple of 4", Hsz);
+    if ((int64_t)S * rows * Hsz > ((int64_t)1 << 40)) return fail(ATTN_ERR_UNSUPPORTED, "S*rows*Hsz too large");
+    if (!aligned16(outs) || !aligned16(out) || ((uintptr_t)lses & 3u) != 0 || ((uintptr_t)lse_out & 3u) != 0)
+        return fail(ATTN_ERR_ALIGN, "outs and out must be 16-byte aligned, lses and lse_out 4-byte aligned");
+    const hipError_t e = attn::launch_merge_shards(outs, lses, S, rows, Hsz, out, lse_out, stream);
+    if (e != hipSuccess) return fail_hip(e, "shard merge kernel launch");
     return ATTN_OK;
 }
 

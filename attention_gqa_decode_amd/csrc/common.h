@@ -23,6 +23,7 @@ struct DecodeParams {
     const uint16_t *k;   // [B][KH][S][Hsz], bf16 or (reinterpreted) FP8 E4M3 bytes
     const uint16_t *v;   // same layout as k
     float *out;          // fp32 [B][Hq][Hsz]
+    float *lse;          // optional fp32 [B][Hq][qlen]: log2 of each row's softmax denominator (NULL = none)
     float *ws;           // partial slots, each slot_floats long
     int *counters;       // arrival counters [2 * kMaxCtas], zero between calls
     int64_t kv_stride;   // S
@@ -64,6 +65,7 @@ struct WideMergeParams {
     const WideHead *head_dev;
     const float *ws;      // partial slots
     float *out;           // fp32 [B][Hq][qlen][Hsz]
+    float *lse;           // optional [B][Hq][qlen]
     int slot_floats;
     int NC, G, Hq, qlen;
     float v_scale;
@@ -97,6 +99,8 @@ struct PlanBase {
 hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int64_t stride, LeanPlan *plan_out,
                               int *wide_count, WideHead *wide, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out,
+                               float *lse_out, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int NC);  // resident decode workgroups per CU
 int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,

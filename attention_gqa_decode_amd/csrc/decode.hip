@@ -366,8 +366,9 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
             O += ov[j] * f;
         }
         // column g: token g / G, head g % G
-        float *dst = p.out + (((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
-        *reinterpret_cast<f32x4 *>(dst) = O * (p.v_scale / L);
+        const int64_t orow = ((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G;
+        *reinterpret_cast<f32x4 *>(p.out + orow * HSZ + 4 * d4) = O * (p.v_scale / L);
+        if (p.lse && d4 == 0) p.lse[orow] = M + __log2f(L);
     }
 }
 
@@ -458,8 +459,9 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const WideMergeParams m
             combine_state(M, L, O, r[0], r[1], f32x4{r[2], r[3], r[4], r[5]});
         }
         // column g: token g / G, head g % G
-        float *dst = mp.out + (((int64_t)b * mp.Hq + kh * G + g % G) * mp.qlen + g / G) * HSZ + col;
-        *reinterpret_cast<f32x4 *>(dst) = O * (mp.v_scale / L);
+        const int64_t orow = ((int64_t)b * mp.Hq + kh * G + g % G) * mp.qlen + g / G;
+        *reinterpret_cast<f32x4 *>(mp.out + orow * HSZ + col) = O * (mp.v_scale / L);
+        if (mp.lse && col == 0) mp.lse[orow] = M + __log2f(L);
     }
 }
 
@@ -641,6 +643,8 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         float *orow = p.out + (int64_t)b * p.Hq * p.qlen * HSZ;
         for (int e = threadIdx.x; e < p.Hq * p.qlen * HSZ / 4; e += W * 64)
             reinterpret_cast<f32x4 *>(orow)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.lse)
+            for (int e = threadIdx.x; e < p.Hq * p.qlen; e += W * 64) p.lse[(int64_t)b * p.Hq * p.qlen + e] = -__builtin_inff();
     }
 
     bool first_piece = true;
@@ -737,8 +741,9 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
             }
             if (whole) {
                 // column g: token g / G, head g % G
-                float *dst = p.out + (((int64_t)pc.b * p.Hq + h0 + g % G) * p.qlen + g / G) * HSZ + 4 * d4;
-                *reinterpret_cast<f32x4 *>(dst) = O * (p.v_scale / Lt);
+                const int64_t orow = ((int64_t)pc.b * p.Hq + h0 + g % G) * p.qlen + g / G;
+                *reinterpret_cast<f32x4 *>(p.out + orow * HSZ + 4 * d4) = O * (p.v_scale / Lt);
+                if (p.lse && d4 == 0) p.lse[orow] = M + __log2f(Lt);
             } else {
                 st_shared_f4(p.ws + so + g * HSZ + 4 * d4, O);
                 if (d4 == 0) {
@@ -860,6 +865,38 @@ hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int6
     return hipGetLastError();
 }
 
+// Merge of S decode outputs over disjoint key ranges of the same rows (KV
+// split across devices or calls): each shard's normalised row O_s comes with
+// lse_s = log2 of its softmax denominator, so the whole row is
+// sum_s O_s 2^(lse_s - M) / sum_s 2^(lse_s - M) with M = max_s lse_s, the same
+// associative rescale as the merge of partial states ("LeanAttention" digest,
+// section "조각별로 합칠 수 있는 정확한 소프트맥스").  Thread per float4 of a
+// row; a shard with lse = -inf (no keys) contributes nothing.
+__global__ __launch_bounds__(256) void merge_shards_kernel(const float *outs, const float *lses, int S, int64_t rows,
+                                                           int Hsz, float *out, float *lse_out) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = Hsz / 4;
+    if (u >= rows * per_row) return;
+    const int64_t r = u / per_row;
+    const int d4 = (int)(u - r * per_row);
+    float M = -__builtin_inff();
+    for (int sh = 0; sh < S; ++sh) M = fmaxf(M, lses[sh * rows + r]);
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != -__builtin_inff()) {
+        for (int sh = 0; sh < S; ++sh) {
+            const float ls = lses[sh * rows + r];
+            if (ls == -__builtin_inff()) continue;
+            const float w = __builtin_amdgcn_exp2f(ls - M);
+            L += w;
+            O += *reinterpret_cast<const f32x4 *>(outs + (sh * rows + r) * Hsz + 4 * d4) * w;
+        }
+        O *= 1.f / L;
+    }
+    *reinterpret_cast<f32x4 *>(out + r * Hsz + 4 * d4) = O;
+    if (lse_out && d4 == 0) lse_out[r] = M == -__builtin_inff() ? M : M + __log2f(L);
+}
+
 // Zero-fills `bytes` (a multiple of 4) with plain vector stores; used for the
 // arrival counters of a freshly allocated workspace.
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, size_t n) {
@@ -872,6 +909,15 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream) {
     size_t blocks = (n + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint32_t *>(ptr), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out,
+                               float *lse_out, hipStream_t stream) {
+    const int64_t n = rows * (Hsz / 4);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_shards_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, outs, lses, S, rows,
+                       Hsz, out, lse_out);
     return hipGetLastError();
 }
 

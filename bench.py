@@ -92,7 +92,7 @@ def log(msg: str) -> None:
 
 
 def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0,
-                 fp8: bool = False, block_size: int = 0, device_seqlens: bool = False):
+                 fp8: bool = False, block_size: int = 0, device_seqlens: bool = False, lse: bool = False):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
     events recorded on the launch stream around every decode-kernel launch (roofline).
     With device_seqlens the lengths sit in a device tensor and the plan is built on the device."""
@@ -108,7 +108,7 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
         q, k, v, sl = W.decode_inputs(shape, device="cuda")
     sl = sl.tolist()
     kv_read = 2 * shape.KH * sum(sl) * shape.Hsz * (1 if fp8 else 2)
-    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(kv_read, 1)))) if rotate else 1
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / max(kv_read, 1)))) if rotate else 1
     ks = [k] + [k.clone() for _ in range(copies - 1)]
     vs = [v] + [v.clone() for _ in range(copies - 1)]
     out = torch.empty((shape.B, shape.Hq, shape.Hsz), dtype=torch.float32, device="cuda")
@@ -121,7 +121,9 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
         torch.cuda.empty_cache()
     else:
         sl_arg = torch.tensor(sl, dtype=torch.int32, device="cuda") if device_seqlens else sl
-        calls = [A.PreparedDecode(q, ks[i], vs[i], sl_arg, out, scale=scale, schedule=schedule) for i in range(copies)]
+        lse_t = torch.empty(shape.B * shape.Hq, dtype=torch.float32, device="cuda") if lse else None
+        calls = [A.PreparedDecode(q, ks[i], vs[i], sl_arg, out, scale=scale, schedule=schedule, out_lse=lse_t)
+                 for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         calls[i % copies](stream)
@@ -161,6 +163,32 @@ def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = 
     del q, ks, vs, out, calls
     torch.cuda.empty_cache()
     return res
+
+
+def bench_merge_shards(S: int, rows: int, Hsz: int, steps: int) -> float:
+    """Time of attn_merge_shards over S shard outputs of `rows` rows (µs per call)."""
+    import torch
+
+    import attention_gqa_decode_amd as A
+
+    outs = torch.randn((S, rows, Hsz), dtype=torch.float32, device="cuda")
+    lses = torch.randn((S, rows), dtype=torch.float32, device="cuda")
+    out = torch.empty((rows, Hsz), dtype=torch.float32, device="cuda")
+    A.attn_merge_shards(outs, lses, out=out)
+    torch.cuda.synchronize()
+    # the calls are captured in a graph: back to back from Python, the host would set the pace
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            A.attn_merge_shards(outs, lses, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps * 1e3
 
 
 def bench_multi(shape, gamma: int, steps: int, warmup: int):
@@ -359,6 +387,7 @@ def main():
     schedules = []
     devseq = []
     multi = None
+    kv_split = None
     tiny = None
     probe = None
     prefill = None
@@ -401,11 +430,20 @@ def main():
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
+        log("KV-sequence split of long_mqa over 8 devices: one shard's decode (with out_lse) and the merge ...")
+        shard = W.DecodeShape("long_mqa_shard8", 1, 8, 1, 128, (262144 // 8,), seed=1003)
+        sh = bench_decode(shard, args.steps, args.warmup, hev, lse=True)
+        merge_us = bench_merge_shards(8, 1 * 8, 128, args.steps)
+        kv_split = {"workload": "long_mqa split 8 ways (B=1, Hq=8, KH=1, L=32768 per shard)",
+                    "shard_us_per_step": round(sh["us_per_step"], 2), "shard_GBps": round(sh["GBps"], 1),
+                    "merge_8_shards_us": round(merge_us, 2)}
+        log(f"  shard {sh['us_per_step']:.1f} us ({sh['GBps']:.0f} GB/s), merge {merge_us:.1f} us")
         log("decode tiny (B=1, Hq=8, KH=2, L=1024: cache-resident, a latency figure only) ...")
         t = bench_decode(W.decode_workload("tiny"), args.steps, args.warmup, hev, rotate=False)
-        tiny = {"workload": "tiny", "us_per_step": round(t["us_per_step"], 2), "kernel_us": round(t["kernel_us"], 2),
-                "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"]}
-        log(f"  {tiny['us_per_step']:.1f} us/step")
+        tiny = {"workload": "tiny", "kernel_us": round(t["kernel_us"], 2),
+                "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"],
+                "back_to_back_us_per_call": round(t["us_per_step"], 2)}
+        log(f"  decode kernel {tiny['kernel_us']:.1f} us; back-to-back calls from Python {tiny['back_to_back_us_per_call']:.1f} us")
         probe = bench_copy_probe(max(3, args.steps // 5))
         log(f"copy probe {probe['copy_read_plus_write_GBps']:.0f} GB/s, read probe {probe['read_GBps']:.0f} GB/s")
     cpu = None
@@ -444,6 +482,7 @@ def main():
         "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,
+        "kv_split": kv_split,
         "tiny_latency": tiny,
         "hbm_probes": probe,
     }

@@ -189,6 +189,12 @@ typedef struct attn_decode_args {
      * beyond the tile count exit at once).  A caller-owned workspace makes the call
      * allocation-free. */
     int seqlens_on_device;
+    /* Optional DEVICE fp32 [B][Hq][q_len] (NULL = none): log2 of each output row's softmax
+     * denominator, sum_j 2^(s_j), with s_j the score in log2 units (scale * k_scale * log2 e
+     * times q.k_j); -inf for a row that sees no key.  With it, decodes over disjoint key
+     * ranges of the same rows (the KV sequence split across devices) merge exactly through
+     * attn_merge_shards. */
+    float *out_lse;
 } attn_decode_args;
 
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
@@ -206,6 +212,22 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas)
 /* The same for multi-token decode with q_len query tokens per request (slots hold
  * G * q_len states); q_len <= 1 gives attn_decode_workspace_bytes. */
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int KH, int Hsz, int q_len, int num_ctas);
+
+/*
+ * attn_merge_shards -- merges S decode outputs of the same rows computed over
+ * disjoint key ranges (the KV sequence split across devices or calls, each run
+ * with out_lse):
+ *   outs     DEVICE fp32 [S][rows][Hsz]   normalised rows of each shard
+ *   lses     DEVICE fp32 [S][rows]        their out_lse (-inf: the shard saw no key)
+ *   out      DEVICE fp32 [rows][Hsz]      sum_s outs[s] 2^(lses[s] - M) / sum_s 2^(lses[s] - M),
+ *                                         M = max_s lses[s]; zero when every lse is -inf
+ *   lse_out  optional DEVICE fp32 [rows]  the merged lse, for a further merge
+ * The rescale-and-sum of the LeanAttention digest's section "조각별로 합칠 수
+ * 있는 정확한 소프트맥스", over shard outputs instead of partial states.  Hsz is
+ * a multiple of 4; outs and out 16-byte aligned.
+ */
+int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out, float *lse_out,
+                      hipStream_t stream);
 
 /*
  * attn_prefill_causal -- causal GQA attention over a whole prompt.

@@ -119,6 +119,7 @@ def ex_args(**kw):
     (dict(block_table=FAKE + 2, block_size=16, max_blocks_per_seq=4, num_blocks=8), A.ATTN_ERR_ALIGN),
     (dict(block_size=16), A.ATTN_ERR_SHAPE),                      # block geometry without a table
     (dict(q_len=-1), A.ATTN_ERR_SHAPE),
+    (dict(out_lse=FAKE + 2), A.ATTN_ERR_ALIGN),
     (dict(q_len=5), A.ATTN_ERR_UNSUPPORTED),                      # G * q_len = 20 > 16 query columns
     (dict(Hq=2, KH=2, q_len=5), A.ATTN_ERR_SHAPE),                 # 4 cached keys < 5 query tokens
     (dict(seqlens=(4, 70), block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8),
@@ -152,6 +153,16 @@ def test_decode_ex_null_args():
 ])
 def test_prefill_argument_checks(args, status):
     assert A.lib().attn_prefill_causal(*args, None) == status
+
+
+def test_merge_shards_argument_checks():
+    lib = A.lib()
+    assert lib.attn_merge_shards(None, FAKE, 2, 8, 128, FAKE, None, None) == A.ATTN_ERR_NULL
+    assert lib.attn_merge_shards(FAKE, FAKE, 0, 8, 128, FAKE, None, None) == A.ATTN_ERR_SHAPE
+    assert lib.attn_merge_shards(FAKE, FAKE, 2, -1, 128, FAKE, None, None) == A.ATTN_ERR_SHAPE
+    assert lib.attn_merge_shards(FAKE, FAKE, 2, 8, 6, FAKE, None, None) == A.ATTN_ERR_SHAPE
+    assert lib.attn_merge_shards(FAKE + 4, FAKE, 2, 8, 128, FAKE, None, None) == A.ATTN_ERR_ALIGN
+    assert lib.attn_merge_shards(FAKE, FAKE + 2, 2, 8, 128, FAKE, None, None) == A.ATTN_ERR_ALIGN
 
 
 def test_copy_probe_argument_checks():
