@@ -7,10 +7,12 @@
 // section "모양이 다른 프리필과 디코드" (parallelism over the query length).
 // Causal, top-left aligned: query row i sees keys 0..i.
 //
-// gfx950 mapping.  A workgroup of 4 wave64s owns 128 query rows of one query
+// gfx950 mapping.  A workgroup of 8 wave64s owns 256 query rows of one query
 // head (32 rows per wave) and walks the K/V blocks of 64 keys up to the
-// diagonal; two workgroups share a CU (256 VGPRs per lane, 74 KiB of LDS each),
-// so one's softmax overlaps the other's matrix products.
+// diagonal; it fills a CU (two waves per SIMD, up to 256 VGPRs per lane, 74 KiB
+// of LDS), so one wave's softmax overlaps its sibling's matrix products, and
+// each staged K/V block serves eight waves (half the staging per product of
+// two 4-wave workgroups).  Waves whose rows end before a block skip it.
 //  * Staging: each block's K (bf16) and V (converted to fp16, exact inside
 //    fp16's normal range) go through registers into one of two LDS stages
 //    while the other stage is being computed: one barrier per block.  K rows
@@ -37,9 +39,9 @@ namespace attn {
 namespace {
 
 constexpr int PF_HSZ = 128;
-constexpr int PF_BM = 128;  // query rows per workgroup
+constexpr int PF_BM = 256;  // query rows per workgroup
 constexpr int PF_BN = 64;   // keys per K/V block
-constexpr int PF_WAVES = 4;
+constexpr int PF_WAVES = 8;
 constexpr int PF_NT = PF_WAVES * 64;
 constexpr int PF_KP = PF_HSZ + 8;   // K stage row pitch (bf16 elements): 272 B
 constexpr int PF_VP = PF_HSZ + 32;  // V stage row pitch (fp16 elements): 320 B
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     uint16_t *__restrict__ out, int B, int ISL, int Hq, int KH, float scale_log2, int nqb) {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_smem[];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: row-block tests stay scalar
     const int l32 = lane & 31, h = lane >> 5;  // query column of the 32x32 tiles, lane half
     const int G = Hq / KH;
 
@@ -141,15 +144,28 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int nkv = last_key / PF_BN + 1;
 
     u32x4 kst[PF_LOADS], vst[PF_LOADS];
+    // Chunk r of a block is the 16-byte word r * PF_NT + tid of its row-major
+    // keys x Hsz slab: a whole block is contiguous, so only the last block of a
+    // ragged ISL needs its rows clamped.
     auto load_block = [&](int kvb) {
+        if (kvb * PF_BN + PF_BN <= ISL) {
+            const uint16_t *kb = kbase + (int64_t)kvb * PF_BN * PF_HSZ + 8 * tid;
+            const uint16_t *vb = vbase + (int64_t)kvb * PF_BN * PF_HSZ + 8 * tid;
 #pragma unroll
-        for (int r = 0; r < PF_LOADS; ++r) {
-            const int idx = r * PF_NT + tid;
-            int key = kvb * PF_BN + idx / PF_CH;
-            key = key < ISL ? key : ISL - 1;
-            const int64_t off = (int64_t)key * PF_HSZ + 8 * (idx % PF_CH);
-            kst[r] = *reinterpret_cast<const u32x4 *>(kbase + off);
-            vst[r] = *reinterpret_cast<const u32x4 *>(vbase + off);
+            for (int r = 0; r < PF_LOADS; ++r) {
+                kst[r] = *reinterpret_cast<const u32x4 *>(kb + r * PF_NT * 8);
+                vst[r] = *reinterpret_cast<const u32x4 *>(vb + r * PF_NT * 8);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < PF_LOADS; ++r) {
+                const int idx = r * PF_NT + tid;
+                int key = kvb * PF_BN + idx / PF_CH;
+                key = key < ISL ? key : ISL - 1;
+                const int64_t off = (int64_t)key * PF_HSZ + 8 * (idx % PF_CH);
+                kst[r] = *reinterpret_cast<const u32x4 *>(kbase + off);
+                vst[r] = *reinterpret_cast<const u32x4 *>(vbase + off);
+            }
         }
     };
     auto store_block = [&](int stage) {
@@ -175,26 +191,43 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
             const uint16_t *ks = pf_smem + stage * PF_STAGE;
             const uint16_t *vs = ks + PF_KSTAGE;
             // ---- BMM1: S^T[key = 32kt + 8(r/4) + 4h + r%4][query l32] ----
-            f32x16 sc[2];
+            // The two key tiles' chains alternate, and the K operand reads run four
+            // ahead of the products that use them, so LDS latency overlaps the MFMAs
+            // instead of sitting between every pair of them.
+            f32x16 sc[2] = {f32x16{}, f32x16{}};
+            bf16x8 kop[PF_HSZ / 16][2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                sc[kt] = f32x16{};
-                const uint16_t *krow = ks + (32 * kt + l32) * PF_KP + 8 * h;
+            for (int s = 0; s < PF_HSZ / 16; ++s)
 #pragma unroll
-                for (int s = 0; s < PF_HSZ / 16; ++s)
-                    sc[kt] = mfma_qk(*reinterpret_cast<const bf16x8 *>(krow + 16 * s), qop[s], sc[kt]);
+                for (int kt = 0; kt < 2; ++kt)
+                    kop[s][kt] = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * PF_KP + 8 * h + 16 * s);
+#pragma unroll
+            for (int s = 0; s < PF_HSZ / 16; ++s)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma_qk(kop[s][kt], qop[s], sc[kt]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+            for (int i = 0; i < 2 * (PF_HSZ / 16) - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             // ---- online softmax (log2 domain, lazy rescale) ----
-            const int row = q0 + l32;
-            const bool diag = key_base + PF_BN - 1 > q0;
+            // Only the blocks that reach past the wave's first row need the causal
+            // mask; the test is uniform over the wave, so the others skip it.
+            if (key_base + PF_BN - 1 > q0) {
+                const int lim = q0 + l32 - key_base - 4 * h;  // key offset limit of this lane's row
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) sc[kt][r] = NEG_INF;
+            }
             float mx = NEG_INF;  // max raw score of this query over the block
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if (diag && key_base + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3) > row) sc[kt][r] = NEG_INF;
-                    mx = fmaxf(mx, sc[kt][r]);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
             // The reference max moves only when the block max exceeds it by more
             // than kLazy (log2 units): the weights then stay <= 2^kLazy, far inside

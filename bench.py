@@ -287,6 +287,34 @@ def bench_copy_probe(steps: int):
             "read_bytes": 4 * n, "read_us": rms * 1e3, "read_GBps": 4 * n / (rms * 1e-3) / 1e9}
 
 
+def bench_read_same_bytes(nbytes: int, reps: int):
+    """The read probe over exactly `nbytes` (a decode workload's K+V bytes), rotated over
+    enough buffers to defeat the last-level cache, timed per launch with events on the
+    launch stream like the decode kernel: the practical read ceiling at that size."""
+    import torch
+
+    import attention_gqa_decode_amd as A
+
+    copies = max(1, math.ceil(ROTATE_BYTES / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    for b in bufs:
+        b.fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        A.attn_hbm_read_probe(b, sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        A.attn_hbm_read_probe(bufs[i % copies], sink)
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "copies_rotated": copies, "kernel_us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+
+
 def cpu_baseline(shape, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on the headline workload (whole steps, repeated)."""
     import oracle
@@ -446,6 +474,21 @@ def main():
         log(f"  decode kernel {tiny['kernel_us']:.1f} us; back-to-back calls from Python {tiny['back_to_back_us_per_call']:.1f} us")
         probe = bench_copy_probe(max(3, args.steps // 5))
         log(f"copy probe {probe['copy_read_plus_write_GBps']:.0f} GB/s, read probe {probe['read_GBps']:.0f} GB/s")
+        # the same read at each decode workload's K+V size, against that workload's decode kernel time
+        kern = {x["workload"]: x for x in [r] + others}
+        probe["same_bytes"] = []
+        for name in ["llama3_8b", "long_mqa"]:
+            if name not in kern:
+                continue
+            d = kern[name]
+            kv = 2 * d["KH"] * d["sum_kvsl"] * d["Hsz"] * 2
+            rp = bench_read_same_bytes(kv, args.steps)
+            rp["workload"] = name
+            rp["decode_kernel_us"] = round(d["kernel_us"], 2)
+            rp["read_probe_over_decode_kernel_time"] = round(rp["kernel_us"] / d["kernel_us"], 3)
+            probe["same_bytes"].append(rp)
+            log(f"  read of {name}'s {kv / 2**20:.0f} MiB of K/V alone: {rp['kernel_us']:.1f} us "
+                f"(decode kernel {d['kernel_us']:.1f} us)")
     cpu = None
     if not args.skip_cpu:
         log("cpu oracle baseline ...")

@@ -48,7 +48,7 @@ def run_and_check(B, ISL, Hq, KH, Hsz, seed, rows=None):
     assert excess.max() <= 0, f"max |err| {np.abs(g - r).max():.3e}"
 
 
-@pytest.mark.parametrize("ISL", [1, 5, 64, 128, 129, 300])
+@pytest.mark.parametrize("ISL", [1, 5, 64, 128, 129, 255, 256, 257, 300, 700])
 def test_small_prompts(ISL):
     note(f"prefill B=2 ISL={ISL} Hq=8 KH=2")
     run_and_check(2, ISL, 8, 2, 128, seed=ISL)
