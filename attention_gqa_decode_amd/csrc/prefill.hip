@@ -41,6 +41,8 @@ namespace {
 constexpr int PF_HSZ = 128;
 constexpr int PF_BM = 256;  // query rows per workgroup
 constexpr int PF_BN = 64;   // keys per K/V block
+constexpr int PF_NKT = PF_BN / 32;  // 32-key tiles of BMM1 per block
+constexpr int PF_NCH = PF_BN / 16;  // 16-key contractions of BMM2 per block
 constexpr int PF_WAVES = 8;
 constexpr int PF_NT = PF_WAVES * 64;
 constexpr int PF_KP = PF_HSZ + 8;   // K stage row pitch (bf16 elements): 272 B
@@ -191,23 +193,25 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
             const uint16_t *ks = pf_smem + stage * PF_STAGE;
             const uint16_t *vs = ks + PF_KSTAGE;
             // ---- BMM1: S^T[key = 32kt + 8(r/4) + 4h + r%4][query l32] ----
-            // The two key tiles' chains alternate, and the K operand reads run four
+            // The key tiles' chains alternate, and the K operand reads run four
             // ahead of the products that use them, so LDS latency overlaps the MFMAs
             // instead of sitting between every pair of them.
-            f32x16 sc[2] = {f32x16{}, f32x16{}};
-            bf16x8 kop[PF_HSZ / 16][2];
+            f32x16 sc[PF_NKT];
+#pragma unroll
+            for (int kt = 0; kt < PF_NKT; ++kt) sc[kt] = f32x16{};
+            bf16x8 kop[PF_HSZ / 16][PF_NKT];
 #pragma unroll
             for (int s = 0; s < PF_HSZ / 16; ++s)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < PF_NKT; ++kt)
                     kop[s][kt] = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * PF_KP + 8 * h + 16 * s);
 #pragma unroll
             for (int s = 0; s < PF_HSZ / 16; ++s)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma_qk(kop[s][kt], qop[s], sc[kt]);
+                for (int kt = 0; kt < PF_NKT; ++kt) sc[kt] = mfma_qk(kop[s][kt], qop[s], sc[kt]);
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
 #pragma unroll
-            for (int i = 0; i < 2 * (PF_HSZ / 16) - 4; ++i) {
+            for (int i = 0; i < PF_NKT * (PF_HSZ / 16) - 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
@@ -218,14 +222,14 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
             if (key_base + PF_BN - 1 > q0) {
                 const int lim = q0 + l32 - key_base - 4 * h;  // key offset limit of this lane's row
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < PF_NKT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) sc[kt][r] = NEG_INF;
             }
             float mx = NEG_INF;  // max raw score of this query over the block
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < PF_NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
             const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
             const int t = lane & 15;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < PF_NCH; ++c) {
                 f16x8 pb;  // P^T operand of chunk c
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
