@@ -8,6 +8,7 @@
 
 #include <map>
 #include <mutex>
+#include <vector>
 #include <string>
 #include <utility>
 
@@ -326,13 +327,21 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (st != ATTN_OK) return st;
     // The selector (the digest's runtime selection policy: stream-K tiles for
     // long, few-head or ragged work; no split when the batch alone fills every
-    // resident slot) picks the fixed split with one CTA per segment when there
-    // are at least twice as many segments as resident workgroups, and stream-K
-    // otherwise.
+    // resident slot evenly) runs one CTA per segment when that finishes no later
+    // than stream-K's even share, ceil(N / resident) tiles (so no partial
+    // states at all), and stream-K otherwise.  With device seqlens the host
+    // cannot see the lengths, and stream-K is the choice that never leaves a
+    // long context to one CTA.
     int schedule = a->schedule;
-    if (schedule == ATTN_SCHEDULE_AUTO)
-        schedule = (int64_t)a->B * a->KH >= 2LL * resident && a->num_ctas == 0 ? ATTN_SCHEDULE_FIXED_SPLIT
-                                                                              : ATTN_SCHEDULE_STREAM_K;
+    if (schedule == ATTN_SCHEDULE_AUTO) {
+        schedule = ATTN_SCHEDULE_STREAM_K;
+        if (!dev_sl && a->num_ctas == 0 && p.plan.N > 0) {
+            std::vector<int64_t> heap((size_t)resident);
+            const int64_t even = (p.plan.N + resident - 1) / resident;
+            if (plan_whole_segments_makespan(p.plan, resident, heap.data()) <= even)
+                schedule = ATTN_SCHEDULE_FIXED_SPLIT;
+        }
+    }
     if (schedule == ATTN_SCHEDULE_FIXED_SPLIT) {
         const int S = a->num_splits > 0 ? a->num_splits
                       : a->schedule == ATTN_SCHEDULE_AUTO ? 1 : default_splits(p.plan, resident);

@@ -156,3 +156,47 @@ ATTN_HD SegmentCtas plan_segment_ctas(const LeanPlan &p, int64_t seg_begin, int6
     s.n = plan_cta_of_tile(p, seg_end - 1) - s.c_lo + 1;
     return s;
 }
+
+// Selector support (host side).  One workgroup per segment, launched in
+// segment order onto R resident slots, each segment taking the slot that
+// frees first (the dispatcher hands out workgroups as slots free up): the
+// makespan in tiles, from a binary min-heap over the slots' finish times.
+// `heap` must hold R entries.  Stream-K's makespan is ceil(N / R) plus its
+// merges, so running every segment whole pays only when this comes out no
+// longer than that: many segments of similar length.  A ragged batch, where
+// a few long contexts finish last, does not ("LeanAttention" digest, section
+// "모양이 다른 프리필과 디코드": fixed splits leave partial waves and idle units).
+inline int64_t plan_whole_segments_makespan(const LeanPlan &p, int R, int64_t *heap) {
+    if (R < 1) R = 1;
+    int used = 0;
+    int64_t makespan = 0;
+    for (int b = 0; b < p.B; ++b) {
+        const int64_t n = plan_tiles_per_segment(p, b);
+        for (int kh = 0; kh < p.KH; ++kh) {
+            int64_t t;
+            if (used < R) {  // a free slot: push its finish time
+                t = n;
+                int i = used++;
+                while (i > 0 && heap[(i - 1) / 2] > t) {
+                    heap[i] = heap[(i - 1) / 2];
+                    i = (i - 1) / 2;
+                }
+                heap[i] = t;
+            } else {  // the earliest slot takes it: replace the root and sift down
+                t = heap[0] + n;
+                int i = 0;
+                for (;;) {
+                    int c = 2 * i + 1;
+                    if (c >= used) break;
+                    if (c + 1 < used && heap[c + 1] < heap[c]) ++c;
+                    if (heap[c] >= t) break;
+                    heap[i] = heap[c];
+                    i = c;
+                }
+                heap[i] = t;
+            }
+            makespan = t > makespan ? t : makespan;
+        }
+    }
+    return makespan;
+}

@@ -413,6 +413,7 @@ def main():
     log(f"  {r['us_per_step']:.1f} us/step, {r['GBps']:.0f} GB/s, kernel {r['kernel_us']:.1f} us")
     others = []
     schedules = []
+    sweep = []
     devseq = []
     multi = None
     kv_split = None
@@ -455,6 +456,15 @@ def main():
             devseq.append({"workload": name, "host_seqlens_us": round(hs["us_per_step"], 2),
                            "device_seqlens_us": round(ds["us_per_step"], 2)})
             log(f"  {name}: host {hs['us_per_step']:.1f} us, device {ds['us_per_step']:.1f} us")
+        log("ragged (G, Hsz) sweep at fixed total KV bytes ...")
+        sweep = []
+        for G in (1, 2, 4, 8, 16):
+            for Hsz in (64, 128, 256):
+                o = bench_decode(W.ragged_sweep_point(G, Hsz), max(10, args.steps // 2), args.warmup, hev)
+                sweep.append({"G": G, "Hsz": Hsz, "KH": o["KH"], "max_kvsl": o["max_kvsl"],
+                              "bytes_per_step": o["bytes_per_step"], "us_per_step": round(o["us_per_step"], 2),
+                              "GBps": round(o["GBps"], 1), "frac_of_peak": round(o["frac_of_peak"], 4)})
+                log(f"  G={G:2d} Hsz={Hsz:3d}: {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
@@ -522,6 +532,7 @@ def main():
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],
         "schedules": schedules,
+        "ragged_sweep_fixed_kv_bytes": sweep,
         "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,

@@ -108,11 +108,13 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
  *                             (the FlashDecoding-style baseline the digest compares
  *                             against, section "모양이 다른 프리필과 디코드");
  *                             num_splits = 0 fills every resident slot once.
- *   ATTN_SCHEDULE_AUTO        the selector: one workgroup per (request, kv head)
- *                             when there are at least twice as many of them as
- *                             resident workgroups (the batch fills the GPU, no
- *                             reduction needed), stream-K otherwise (section
- *                             "런타임 선택 정책").
+ *   ATTN_SCHEDULE_AUTO        the selector: one workgroup per (request, kv head),
+ *                             with no reduction, when running the segments whole
+ *                             in launch order on the resident workgroups ends no
+ *                             later than stream-K's even share of the tiles (many
+ *                             segments of similar length); stream-K otherwise,
+ *                             and always with device seqlens, whose lengths the
+ *                             host cannot see (section "런타임 선택 정책").
  * All schedules compute the same function; results differ only by fp32 rounding.
  */
 #define ATTN_SCHEDULE_AUTO 0

@@ -111,5 +111,12 @@ int harness_segment_ctas(const int32_t *seqlens, int B, int KH, int T, int P, in
     }
     return wide;
 }
+
+// The selector's makespan of one workgroup per segment over R resident slots.
+int64_t harness_whole_segments_makespan(const int32_t *seqlens, int B, int KH, int T, int R) {
+    LeanPlan p = make_plan(seqlens, B, KH, T, R, 0);
+    std::vector<int64_t> heap(R > 0 ? R : 1);
+    return plan_whole_segments_makespan(p, R, heap.data());
+}
 }
 

@@ -36,6 +36,9 @@ def harness(tmp_path_factory):
     lib.harness_cta_begin.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
     lib.harness_cta_of_tile.restype = ctypes.c_int
     lib.harness_cta_of_tile.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64]
+    lib.harness_whole_segments_makespan.restype = ctypes.c_int64
+    lib.harness_whole_segments_makespan.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int]
     lib.harness_merge_slots.restype = ctypes.c_int
     lib.harness_merge_slots.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
@@ -281,3 +284,54 @@ def test_stream_k_ranges_at_the_limits(harness, N, P):
     for t in sorted(ts):
         c = harness.harness_cta_of_tile(N, P, t)
         assert c * N // P <= t < (c + 1) * N // P, (t, c)
+
+
+# ------------------------------------------------------------------ selector
+
+
+def makespan(harness, sl, KH, T, R):
+    sl = np.ascontiguousarray(sl, dtype=np.int32)
+    return harness.harness_whole_segments_makespan(sl.ctypes.data, len(sl), KH, T, R)
+
+
+def makespan_naive(sl, KH, T, R):
+    """Segments in order, each onto the slot that frees first (lowest index on ties)."""
+    slots = [0] * R
+    end = 0
+    for L in sl:
+        n = -(-int(L) // T)
+        for _ in range(KH):
+            i = min(range(R), key=lambda j: slots[j])
+            slots[i] += n
+            end = max(end, slots[i])
+    return end
+
+
+def test_whole_segments_makespan_matches_a_naive_dispatch(harness):
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        B = int(rng.integers(1, 40))
+        KH = int(rng.integers(1, 9))
+        T = int(rng.choice([16, 64, 256]))
+        R = int(rng.integers(1, 70))
+        sl = rng.integers(0, 3000, B)
+        assert makespan(harness, sl, KH, T, R) == makespan_naive(sl, KH, T, R), (B, KH, T, R)
+
+
+def test_selector_rule_on_the_shapes_that_decide_it(harness):
+    """Whole segments (no partial states) only when they finish within stream-K's even share."""
+    from attention_gqa_decode_amd import workloads as W
+
+    def whole_wins(sl, KH, T, R):
+        N = sum(KH * (-(-int(L) // T)) for L in sl)
+        return makespan(harness, sl, KH, T, R) <= -(-N // R)
+
+    # many short uniform requests: every slot gets the same number of segments
+    assert whole_wins([300] * 256, 8, 256, 512)
+    # the ragged batch and its (G, Hsz) sweep points: a few long contexts would finish last
+    for G in (1, 2, 4, 8, 16):
+        for Hsz, T, R in ((64, 256, 512), (128, 256, 256), (256, 128, 256)):
+            s = W.ragged_sweep_point(G, Hsz)
+            assert not whole_wins(s.seqlens, s.KH, T, R), (G, Hsz)
+    # a uniform long batch with fewer segments than slots leaves slots idle
+    assert not whole_wins([8192] * 16, 8, 256, 256)
