@@ -154,7 +154,10 @@ typedef struct attn_decode_args {
     size_t workspace_bytes;   /* its size; must be >= attn_decode_workspace_bytes(...) */
     int tile_keys;            /* LeanTile size T in keys; 0 = library default */
     int num_ctas;             /* stream-K: number of persistent workgroups P, <= ATTN_MAX_CTAS;
-                                 0 = all resident slots.  Must be 0 for the fixed split. */
+                                 0 = the library's choice: every resident slot once, or
+                                 k times (k = floor(B*KH / slots), at most 4) when the
+                                 (request, kv head) segments outnumber the slots at
+                                 least twice.  Must be 0 for the fixed split. */
     hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the decode kernel */
     hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel (before the
                                  merge kernel of heads split over more than 16 workgroups) */
@@ -187,7 +190,7 @@ typedef struct attn_decode_args {
      * then be given (> 0) unless a block table is; each L_b is clamped into
      * [0, kv_stride] (or the table's capacity) on the device, and a nonzero L_b below
      * q_len gives undefined rows for that request.  Such a call always needs the
-     * workspace, and with num_ctas = 0 it launches every resident workgroup (those
+     * workspace, and with num_ctas = 0 it launches the default workgroup count (those
      * beyond the tile count exit at once).  A caller-owned workspace makes the call
      * allocation-free. */
     int seqlens_on_device;

@@ -238,6 +238,26 @@ def test_auto_schedule_many_segments():
     assert np.abs(got - sk).max() <= 1e-5
 
 
+def test_default_ctas_many_segments():
+    # 64 requests x 32 kv heads (G=1): far more segments than resident workgroups, so the
+    # default stream-K launch runs several workgroups per slot.  A workspace sized with
+    # num_ctas = 0 must cover that call, and the result matches the oracle and a launch of
+    # one workgroup per slot.
+    rng = np.random.default_rng(31)
+    sl = rng.integers(1, 3000, 64).tolist()
+    note(f"decode default CTAs, B=64 KH=32 G=1, sum(L)={sum(sl)}")
+    q, k, v, sl = inputs(64, 32, 32, 128, sl, seed=31)
+    need = A.attn_decode_workspace_bytes(64, 32, 32, 128, 0)
+    assert need > A.attn_decode_workspace_bytes(64, 32, 32, 128, 256)
+    ws = torch.zeros(need // 4 + 1, dtype=torch.int32, device="cuda")
+    rows = np.random.default_rng(32).choice(64 * 32, 256, replace=False)
+    err, got = decode_err(q, k, v, sl, rows=rows, workspace=ws, schedule=A.ATTN_SCHEDULE_STREAM_K)
+    note(f"  max err {err:.3e}")
+    assert err <= DECODE_TOL
+    one = gpu_decode(q, k, v, sl, schedule=A.ATTN_SCHEDULE_STREAM_K, num_ctas=256)
+    assert np.abs(got - one).max() <= 1e-5
+
+
 @pytest.mark.parametrize("name", ["long_mqa", "ragged"])
 def test_fixed_split_full_size(name):
     s = W.decode_workload(name)
