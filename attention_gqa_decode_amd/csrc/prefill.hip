@@ -38,20 +38,26 @@
 namespace attn {
 namespace {
 
-constexpr int PF_HSZ = 128;
 constexpr int PF_BM = 256;  // query rows per workgroup
 constexpr int PF_BN = 64;   // keys per K/V block
 constexpr int PF_NKT = PF_BN / 32;  // 32-key tiles of BMM1 per block
 constexpr int PF_NCH = PF_BN / 16;  // 16-key contractions of BMM2 per block
 constexpr int PF_WAVES = 8;
 constexpr int PF_NT = PF_WAVES * 64;
-constexpr int PF_KP = PF_HSZ + 8;   // K stage row pitch (bf16 elements): 272 B
-constexpr int PF_VP = PF_HSZ + 32;  // V stage row pitch (fp16 elements): 320 B
-constexpr int PF_KSTAGE = PF_BN * PF_KP;  // elements
-constexpr int PF_VSTAGE = PF_BN * PF_VP;
-constexpr int PF_STAGE = PF_KSTAGE + PF_VSTAGE;
-constexpr int PF_CH = PF_HSZ / 8;                  // 16-byte chunks per row
-constexpr int PF_LOADS = PF_BN * PF_CH / PF_NT;    // 16-byte chunks per thread per block (K, and again V)
+// Sizes that follow the head dimension (64 or 128).  The row pitches keep
+// the operand reads conflict-free: K rows of 16 B more than a row (row-parallel
+// 16-byte reads), V rows of 64 B more (the transposed reads of four rows).
+template <int HSZ>
+struct PfDims {
+    static constexpr int KP = HSZ + 8;               // K stage row pitch (bf16 elements): 144 or 272 B
+    static constexpr int VP = HSZ + 32;              // V stage row pitch (fp16 elements): 192 or 320 B
+    static constexpr int KSTAGE = PF_BN * KP;        // elements
+    static constexpr int VSTAGE = PF_BN * VP;
+    static constexpr int STAGE = KSTAGE + VSTAGE;
+    static constexpr int CH = HSZ / 8;               // 16-byte chunks per row
+    static constexpr int LOADS = PF_BN * CH / PF_NT; // 16-byte chunks per thread per block (K, and again V)
+    static_assert(PF_BN * CH % PF_NT == 0, "a block's chunks split evenly over the threads");
+};
 constexpr int PF_XCDS = 8;
 constexpr float kLazy = 8.f;  // lazy-rescale threshold in log2 units (weights <= 256)
 
@@ -85,14 +91,20 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 &w) {
 // each 16-lane block, lane t reads 8 bytes at row key0 + t/4, columns
 // d0 + 4 (t % 4) .. +3; the transposing read then hands lane i the column
 // d0 + i at rows key0 .. key0+3.
+template <int VP>
 __device__ __forceinline__ i16x4 v_cols(const uint16_t *vstage, int key0, int d0, int t) {
-    const uint16_t *p = vstage + (key0 + (t >> 2)) * PF_VP + d0 + 4 * (t & 3);
+    const uint16_t *p = vstage + (key0 + (t >> 2)) * VP + d0 + 4 * (t & 3);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
 }
 
+template <int HSZ>
 __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, int B, int ISL, int Hq, int KH, float scale_log2, int nqb) {
+    using D = PfDims<HSZ>;
+    constexpr int PF_HSZ = HSZ;
+    constexpr int PF_KP = D::KP, PF_VP = D::VP, PF_KSTAGE = D::KSTAGE, PF_STAGE = D::STAGE;
+    constexpr int PF_CH = D::CH, PF_LOADS = D::LOADS;
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -267,8 +279,8 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
                 for (int dt = 0; dt < PF_HSZ / 32; ++dt) {
                     const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
-                    const i16x4 lo = v_cols(vs, 16 * c + 4 * h, d0, t);
-                    const i16x4 hi = v_cols(vs, 16 * c + 8 + 4 * h, d0, t);
+                    const i16x4 lo = v_cols<PF_VP>(vs, 16 * c + 4 * h, d0, t);
+                    const i16x4 hi = v_cols<PF_VP>(vs, 16 * c + 8 + 4 * h, d0, t);
                     const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[dt] = mfma_pv(a, pb, oacc[dt]);
                 }
@@ -298,24 +310,37 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void
 
 }  // namespace
 
-hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
-                                 int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
-                                 hipStream_t stream) {
-    if (Hsz != PF_HSZ) return hipErrorInvalidValue;
+namespace {
+
+template <int HSZ>
+hipError_t launch_prefill_h(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, int B, int ISL,
+                            int Hq, int KH, float scale_log2, hipStream_t stream) {
     const int nqb = (ISL + PF_BM - 1) / PF_BM;
     const int64_t nblocks = (int64_t)nqb * B * Hq;
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-    const size_t lds = (size_t)2 * PF_STAGE * sizeof(uint16_t);
+    const size_t lds = (size_t)2 * PfDims<HSZ>::STAGE * sizeof(uint16_t);
     static bool attr_set = false;  // above the default dynamic-LDS limit (gfx950 has 160 KiB per CU)
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_causal_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_causal_kernel<HSZ>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(prefill_causal_kernel, dim3((unsigned)nblocks), dim3(PF_NT), lds, stream, q, k, v, out, B, ISL,
-                       Hq, KH, scale_log2, nqb);
+    hipLaunchKernelGGL(prefill_causal_kernel<HSZ>, dim3((unsigned)nblocks), dim3(PF_NT), lds, stream, q, k, v, out, B,
+                       ISL, Hq, KH, scale_log2, nqb);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
+                                 int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
+                                 hipStream_t stream) {
+    switch (Hsz) {
+        case 64: return launch_prefill_h<64>(q, k, v, out, B, ISL, Hq, KH, scale_log2, stream);
+        case 128: return launch_prefill_h<128>(q, k, v, out, B, ISL, Hq, KH, scale_log2, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace attn

@@ -224,7 +224,7 @@ def bench_multi(shape, gamma: int, steps: int, warmup: int):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes_per_step": nbytes}
 
 
-def bench_prefill(steps: int, warmup: int):
+def bench_prefill(steps: int, warmup: int, Hsz: int = 128):
     import torch
 
     import attention_gqa_decode_amd as A
@@ -232,6 +232,8 @@ def bench_prefill(steps: int, warmup: int):
     from attention_gqa_decode_amd import workloads as W
 
     s = W.prefill_workload()
+    if Hsz != s.Hsz:  # the same prompt and heads at another head dimension
+        s = W.PrefillShape(f"prefill_hsz{Hsz}", s.B, s.ISL, s.Hq, s.KH, Hsz, seed=s.seed + Hsz)
     q, k, v = W.prefill_inputs(s, device="cuda")
     out = torch.empty_like(q)
     for _ in range(warmup):
@@ -248,7 +250,7 @@ def bench_prefill(steps: int, warmup: int):
     tf = fl / (ms * 1e-3) / 1e12
     del q, k, v, out
     torch.cuda.empty_cache()
-    return {"workload": "prefill_causal", "B": s.B, "ISL": s.ISL, "Hq": s.Hq, "KH": s.KH, "Hsz": s.Hsz,
+    return {"workload": "prefill_causal" if Hsz == 128 else f"prefill_causal_hsz{Hsz}", "B": s.B, "ISL": s.ISL, "Hq": s.Hq, "KH": s.KH, "Hsz": s.Hsz,
             "flops_per_step": fl, "us_per_step": ms * 1e3, "TFLOPs": tf, "mfma_frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
 
 
@@ -420,6 +422,7 @@ def main():
     tiny = None
     probe = None
     prefill = None
+    prefill64 = None
     if not args.headline_only:
         for name in [n for n in ["llama3_8b", "long_mqa", "long_mqa_x8", "ragged"] if n != head.name]:
             log(f"decode {name} ...")
@@ -468,6 +471,9 @@ def main():
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
+        log("prefill at head dim 64 (same prompt and heads) ...")
+        prefill64 = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2), Hsz=64)
+        log(f"  {prefill64['us_per_step']:.1f} us/step, {prefill64['TFLOPs']:.1f} TFLOP/s")
         log("KV-sequence split of long_mqa over 8 devices: one shard's decode (with out_lse) and the merge ...")
         shard = W.DecodeShape("long_mqa_shard8", 1, 8, 1, 128, (262144 // 8,), seed=1003)
         sh = bench_decode(shard, args.steps, args.warmup, hev, lse=True)
@@ -536,6 +542,7 @@ def main():
         "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,
+        "prefill_hsz64": prefill64,
         "kv_split": kv_split,
         "tiny_latency": tiny,
         "hbm_probes": probe,
