@@ -508,7 +508,8 @@ int attn_prefill_causal(const void *q, const void *k, const void *v, int B, int 
     if (B <= 0 || ISL < 0 || Hq <= 0 || KH <= 0)
         return fail(ATTN_ERR_SHAPE, "B, Hq, KH must be positive and ISL non-negative");
     if (Hq % KH != 0) return fail(ATTN_ERR_SHAPE, "Hq=%d is not a multiple of KH=%d", Hq, KH);
-    if (Hsz != 64 && Hsz != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill supports Hsz=64 and 128 (got %d)", Hsz);
+    if (Hsz != 64 && Hsz != 128 && Hsz != 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill supports Hsz=64, 128 and 256 (got %d)", Hsz);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(ATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
     if (ISL == 0) return ATTN_OK;

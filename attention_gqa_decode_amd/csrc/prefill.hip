@@ -38,25 +38,29 @@
 namespace attn {
 namespace {
 
-constexpr int PF_BM = 256;  // query rows per workgroup
 constexpr int PF_BN = 64;   // keys per K/V block
 constexpr int PF_NKT = PF_BN / 32;  // 32-key tiles of BMM1 per block
 constexpr int PF_NCH = PF_BN / 16;  // 16-key contractions of BMM2 per block
-constexpr int PF_WAVES = 8;
-constexpr int PF_NT = PF_WAVES * 64;
-// Sizes that follow the head dimension (64 or 128).  The row pitches keep
+// Sizes that follow the head dimension (64, 128 or 256).  The row pitches keep
 // the operand reads conflict-free: K rows of 16 B more than a row (row-parallel
-// 16-byte reads), V rows of 64 B more (the transposed reads of four rows).
+// 16-byte reads), V rows of 64 B more (the transposed reads of four rows).  At
+// 256 a wave's Q^T and O^T alone take 192 registers per lane, so the workgroup
+// is 4 waves with one wave per SIMD (512 registers each, AGPRs included) and
+// owns 128 query rows; otherwise 8 waves, two per SIMD, own 256 rows.
 template <int HSZ>
 struct PfDims {
+    static constexpr int WAVES = HSZ == 256 ? 4 : 8;
+    static constexpr int WPE = HSZ == 256 ? 1 : 2;    // waves per SIMD
+    static constexpr int NT = WAVES * 64;
+    static constexpr int BM = 32 * WAVES;             // query rows per workgroup
     static constexpr int KP = HSZ + 8;               // K stage row pitch (bf16 elements): 144 or 272 B
     static constexpr int VP = HSZ + 32;              // V stage row pitch (fp16 elements): 192 or 320 B
     static constexpr int KSTAGE = PF_BN * KP;        // elements
     static constexpr int VSTAGE = PF_BN * VP;
     static constexpr int STAGE = KSTAGE + VSTAGE;
     static constexpr int CH = HSZ / 8;               // 16-byte chunks per row
-    static constexpr int LOADS = PF_BN * CH / PF_NT; // 16-byte chunks per thread per block (K, and again V)
-    static_assert(PF_BN * CH % PF_NT == 0, "a block's chunks split evenly over the threads");
+    static constexpr int LOADS = PF_BN * CH / NT;    // 16-byte chunks per thread per block (K, and again V)
+    static_assert(PF_BN * CH % NT == 0, "a block's chunks split evenly over the threads");
 };
 constexpr int PF_XCDS = 8;
 constexpr float kLazy = 8.f;  // lazy-rescale threshold in log2 units (weights <= 256)
@@ -98,13 +102,15 @@ __device__ __forceinline__ i16x4 v_cols(const uint16_t *vstage, int key0, int d0
 }
 
 template <int HSZ>
-__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal_kernel(
+__global__ __launch_bounds__(PfDims<HSZ>::NT) __attribute__((amdgpu_waves_per_eu(PfDims<HSZ>::WPE)))
+void prefill_causal_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, int B, int ISL, int Hq, int KH, float scale_log2, int nqb) {
     using D = PfDims<HSZ>;
     constexpr int PF_HSZ = HSZ;
     constexpr int PF_KP = D::KP, PF_VP = D::VP, PF_KSTAGE = D::KSTAGE, PF_STAGE = D::STAGE;
     constexpr int PF_CH = D::CH, PF_LOADS = D::LOADS;
+    constexpr int PF_NT = D::NT, PF_BM = D::BM;
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -315,7 +321,7 @@ namespace {
 template <int HSZ>
 hipError_t launch_prefill_h(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, int B, int ISL,
                             int Hq, int KH, float scale_log2, hipStream_t stream) {
-    const int nqb = (ISL + PF_BM - 1) / PF_BM;
+    const int nqb = (ISL + PfDims<HSZ>::BM - 1) / PfDims<HSZ>::BM;
     const int64_t nblocks = (int64_t)nqb * B * Hq;
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = (size_t)2 * PfDims<HSZ>::STAGE * sizeof(uint16_t);
@@ -326,7 +332,7 @@ hipError_t launch_prefill_h(const uint16_t *q, const uint16_t *k, const uint16_t
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(prefill_causal_kernel<HSZ>, dim3((unsigned)nblocks), dim3(PF_NT), lds, stream, q, k, v, out, B,
+    hipLaunchKernelGGL(prefill_causal_kernel<HSZ>, dim3((unsigned)nblocks), dim3(PfDims<HSZ>::NT), lds, stream, q, k, v, out, B,
                        ISL, Hq, KH, scale_log2, nqb);
     return hipGetLastError();
 }
@@ -339,6 +345,7 @@ hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uin
     switch (Hsz) {
         case 64: return launch_prefill_h<64>(q, k, v, out, B, ISL, Hq, KH, scale_log2, stream);
         case 128: return launch_prefill_h<128>(q, k, v, out, B, ISL, Hq, KH, scale_log2, stream);
+        case 256: return launch_prefill_h<256>(q, k, v, out, B, ISL, Hq, KH, scale_log2, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -422,7 +422,7 @@ def main():
     tiny = None
     probe = None
     prefill = None
-    prefill64 = None
+    prefill_dims = []
     if not args.headline_only:
         for name in [n for n in ["llama3_8b", "long_mqa", "long_mqa_x8", "ragged"] if n != head.name]:
             log(f"decode {name} ...")
@@ -471,9 +471,12 @@ def main():
         log("prefill ...")
         prefill = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2))
         log(f"  {prefill['us_per_step']:.1f} us/step, {prefill['TFLOPs']:.1f} TFLOP/s")
-        log("prefill at head dim 64 (same prompt and heads) ...")
-        prefill64 = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2), Hsz=64)
-        log(f"  {prefill64['us_per_step']:.1f} us/step, {prefill64['TFLOPs']:.1f} TFLOP/s")
+        prefill_dims = []
+        for hd in (64, 256):
+            log(f"prefill at head dim {hd} (same prompt and heads) ...")
+            o = bench_prefill(max(3, args.steps // 5), max(1, args.warmup // 2), Hsz=hd)
+            prefill_dims.append(o)
+            log(f"  {o['us_per_step']:.1f} us/step, {o['TFLOPs']:.1f} TFLOP/s")
         log("KV-sequence split of long_mqa over 8 devices: one shard's decode (with out_lse) and the merge ...")
         shard = W.DecodeShape("long_mqa_shard8", 1, 8, 1, 128, (262144 // 8,), seed=1003)
         sh = bench_decode(shard, args.steps, args.warmup, hev, lse=True)
@@ -542,7 +545,7 @@ def main():
         "device_seqlens": devseq,
         "multi_token": multi,
         "prefill": prefill,
-        "prefill_hsz64": prefill64,
+        "prefill_other_head_dims": prefill_dims,
         "kv_split": kv_split,
         "tiny_latency": tiny,
         "hbm_probes": probe,

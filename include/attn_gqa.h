@@ -248,7 +248,7 @@ int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows,
  * the softmax weights rounded to fp16.
  * Source: co-design page, sections "프리필과 디코드의 차이" and "FlashAttention과
  * GEMM 모양" (prefill is the large, compute-bound matmul form of the same
- * fused kernel).  Hsz must be 64 or 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ * fused kernel).  Hsz must be 64, 128 or 256 (ATTN_ERR_UNSUPPORTED otherwise).
  */
 int attn_prefill_causal(const void *q, const void *k, const void *v, int B, int ISL, int Hq, int KH,
                         int Hsz, void *out, hipStream_t stream);

@@ -147,7 +147,7 @@ def test_decode_ex_null_args():
     ((FAKE, FAKE, FAKE, 0, 16, 8, 2, 128, FAKE), A.ATTN_ERR_SHAPE),
     ((FAKE, FAKE, FAKE, 1, -1, 8, 2, 128, FAKE), A.ATTN_ERR_SHAPE),
     ((FAKE, FAKE, FAKE, 1, 16, 8, 3, 128, FAKE), A.ATTN_ERR_SHAPE),
-    ((FAKE, FAKE, FAKE, 1, 16, 8, 2, 256, FAKE), A.ATTN_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, 1, 16, 8, 2, 512, FAKE), A.ATTN_ERR_UNSUPPORTED),
     ((FAKE, FAKE, FAKE, 1, 16, 8, 2, 96, FAKE), A.ATTN_ERR_UNSUPPORTED),
     ((FAKE + 2, FAKE, FAKE, 1, 16, 8, 2, 128, FAKE), A.ATTN_ERR_ALIGN),
     ((FAKE, FAKE, FAKE, 1, 0, 8, 2, 128, FAKE), A.ATTN_OK),  # empty prompt: nothing to do, no launch

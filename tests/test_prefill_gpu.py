@@ -54,16 +54,18 @@ def test_small_prompts(ISL):
     run_and_check(2, ISL, 8, 2, 128, seed=ISL)
 
 
-@pytest.mark.parametrize("ISL", [1, 63, 64, 255, 256, 257, 700])
-def test_head_dim_64(ISL):
-    note(f"prefill Hsz=64 B=2 ISL={ISL} Hq=8 KH=2")
-    run_and_check(2, ISL, 8, 2, 64, seed=640 + ISL)
+@pytest.mark.parametrize("Hsz", [64, 256])
+@pytest.mark.parametrize("ISL", [1, 63, 64, 127, 129, 255, 256, 257, 700])
+def test_other_head_dims(ISL, Hsz):
+    note(f"prefill Hsz={Hsz} B=2 ISL={ISL} Hq=8 KH=2")
+    run_and_check(2, ISL, 8, 2, Hsz, seed=640 + ISL + Hsz)
 
 
-def test_head_dim_64_long_sampled_rows():
-    s = W.PrefillShape("t", 1, 4096, 16, 4, 64, seed=64)
-    note(f"prefill Hsz=64 B=1 ISL={s.ISL} Hq={s.Hq} KH={s.KH}, sampled rows")
-    rng = np.random.default_rng(64)
+@pytest.mark.parametrize("Hsz", [64, 256])
+def test_other_head_dims_long_sampled_rows(Hsz):
+    s = W.PrefillShape("t", 1, 4096, 16, 4, Hsz, seed=Hsz)
+    note(f"prefill Hsz={Hsz} B=1 ISL={s.ISL} Hq={s.Hq} KH={s.KH}, sampled rows")
+    rng = np.random.default_rng(Hsz)
     picks = list(range(0, 32)) + list(range(s.ISL - 32, s.ISL)) + rng.choice(s.ISL, 32, replace=False).tolist()
     rows = np.array([h * s.ISL + i for h in (0, 7, 15) for i in picks])
     run_and_check(s.B, s.ISL, s.Hq, s.KH, s.Hsz, seed=s.seed, rows=rows)
