@@ -13,9 +13,12 @@ previous step.
 
 The same run also times: the decode kernel alone (HIP events recorded on the launch
 stream around each launch -> the ``roofline`` object), the other decode workloads
-(long-context MQA with x1 and x8 scores, the ragged batch), causal prefill (MFMA
-TFLOP/s), a copy and a read of known size (the practical streaming ceiling), and the
-fp64 CPU oracle on the headline workload (``cpu_baseline``).  One JSON line goes to
+(long-context MQA with x1 and x8 scores, the ragged batch, FP8 and paged caches,
+multi-token decode), stream-K against the fixed split, device against host lengths, the
+ragged (G, Hsz) sweep at fixed total KV bytes, causal prefill (MFMA TFLOP/s) at head
+dimensions 128, 64 and 256, one KV-sequence shard and the shard merge, a copy and a read
+of known size (the practical streaming ceiling, also at each decode workload's K+V
+bytes), and the fp64 CPU oracle on the headline workload (``cpu_baseline``).  One JSON line goes to
 stdout; progress goes to stderr.
 """
 from __future__ import annotations
