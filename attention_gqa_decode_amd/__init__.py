@@ -21,7 +21,8 @@ ATTN_ERR_ALIGN = -4
 ATTN_ERR_WORKSPACE = -5
 ATTN_ERR_HIP = -6
 ATTN_MAX_BATCH = 256
-ATTN_MAX_GROUP = 16
+ATTN_MAX_COLUMNS = 64
+ATTN_MAX_COLUMN_ELEMS = 8192
 ATTN_MAX_CTAS = 4096
 ATTN_DECODE_COUNTER_BYTES = 32768
 ATTN_DECODE_PLAN_BYTES = 8192
@@ -152,6 +153,83 @@ def _seqlens_arg(seqlens, B):
     return sl.ctypes.data, 0, sl
 
 
+def _f32_cuda(name, t, shape):
+    """`t` must be a contiguous fp32 CUDA tensor of the given shape (the library writes it)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous fp32 CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _decode_args(q, k_cache, v_cache, seqlens, out, *, q_len, multi, paged, block_table, scale, tile_keys, num_ctas,
+                 schedule, num_splits, k_scale, v_scale, out_lse, workspace):
+    """Checks the tensors of one decode call and packs its attn_decode_args.
+
+    Returns (args, keep): `keep` holds the objects whose memory the packed pointers refer to.
+    q is [B][Hq][Hsz], or [B][Hq][q_len][Hsz] with `multi`; contiguous caches are
+    [B][KH][S][Hsz], paged pools [num_blocks][KH][block_size][Hsz] with an int32 CUDA
+    block_table [B][max_blocks]."""
+    import torch
+    _bf16_cuda("q", q)
+    kv_dtype = _kv_cuda("k_cache", k_cache)
+    if _kv_cuda("v_cache", v_cache) != kv_dtype:
+        raise TypeError("k_cache and v_cache must have the same element type")
+    if not multi:
+        if q.dim() != 3:
+            raise ValueError("q must be [B][Hq][Hsz]")
+        B, Hq, Hsz = q.shape
+    else:
+        if q.dim() != 4 or q.shape[2] != q_len:
+            raise ValueError("q must be [B][Hq][q_len][Hsz]")
+        B, Hq, _, Hsz = q.shape
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[3] != Hsz:
+        raise ValueError("k_cache/v_cache must share one 4-d shape ending in Hsz")
+    KH = k_cache.shape[1]
+    if paged:
+        if block_table.dtype != torch.int32 or not block_table.is_cuda or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous int32 CUDA tensor")
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("pools must be [num_blocks][KH][block_size][Hsz], block_table [B][max_blocks]")
+    elif k_cache.shape[0] != B:
+        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
+    out_shape = (B, Hq, q_len, Hsz) if multi else (B, Hq, Hsz)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.float32, device=q.device)
+    _f32_cuda("out", out, out_shape)
+    sl_ptr, on_dev, sl_keep = _seqlens_arg(seqlens, B)
+    a = attn_decode_args()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
+    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
+    a.scale = float(scale)
+    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+    a.schedule, a.num_splits = int(schedule), int(num_splits)
+    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
+    a.q_len = q_len if q_len > 1 else 0
+    keep = [sl_keep, out]
+    if paged:
+        a.kv_stride = 0
+        a.block_table = block_table.data_ptr()
+        a.block_size, a.max_blocks_per_seq, a.num_blocks = k_cache.shape[2], block_table.shape[1], k_cache.shape[0]
+        keep.append(block_table)
+    else:
+        a.kv_stride = k_cache.shape[2]
+    if out_lse is not None:
+        _f32_cuda("out_lse", out_lse, tuple(out_lse.shape))
+        if out_lse.numel() != B * Hq * q_len:
+            raise ValueError(f"out_lse must hold B*Hq*q_len = {B * Hq * q_len} entries")
+        a.out_lse = out_lse.data_ptr()
+        keep.append(out_lse)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous CUDA tensor")
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        keep.append(workspace)
+    return a, keep
+
+
 def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
     """Decode step (``attn_decode``): q [B][Hq][Hsz], caches [B][KH][S][Hsz] bf16, S = max seqlens.
 
@@ -171,6 +249,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, out=None, stream=None):
         raise ValueError("attn_decode packs the cache to max(seqlens); use attn_decode_ex for another capacity")
     if out is None:
         out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
+    _f32_cuda("out", out, (B, Hq, Hsz))
     _check(lib().attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), sl.ctypes.data, B, Hq, KH, Hsz,
                              out.data_ptr(), _stream_handle(stream)))
     return out
@@ -187,40 +266,17 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     ``workspace`` is an optional CUDA tensor used as the partial-state buffer; its first
     ``ATTN_DECODE_COUNTER_BYTES`` bytes must be zero before its first use (allocate it with
     ``torch.zeros``), and each call leaves them zero.  ``ev_tiles_begin/end`` are optional
-    raw ``hipEvent_t`` handles (ints) recorded around the decode kernel.
+    raw ``hipEvent_t`` handles (ints) bound to the start of the tile kernel and the end of
+    the call's last decode kernel.  ``out_lse`` (optional) is an fp32 CUDA tensor of B*Hq entries.
     """
-    import torch
-    _bf16_cuda("q", q)
-    kv_dtype = _kv_cuda("k_cache", k_cache)
-    if _kv_cuda("v_cache", v_cache) != kv_dtype:
-        raise TypeError("k_cache and v_cache must have the same element type")
-    B, Hq, Hsz = q.shape
-    KH, S = k_cache.shape[1], k_cache.shape[2]
-    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
-    if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
-    if out is None:
-        out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
-    a = attn_decode_args()
-    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
-    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
-    a.kv_stride = S
-    a.scale = float(scale)
-    if workspace is not None:
-        a.workspace = workspace.data_ptr()
-        a.workspace_bytes = workspace.numel() * workspace.element_size()
-    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
+    a, _keep = _decode_args(q, k_cache, v_cache, seqlens, out, q_len=1, multi=False, paged=False, block_table=None,
+                            scale=scale, tile_keys=tile_keys, num_ctas=num_ctas, schedule=schedule,
+                            num_splits=num_splits, k_scale=k_scale, v_scale=v_scale, out_lse=out_lse,
+                            workspace=workspace)
     a.ev_tiles_begin = ev_tiles_begin
     a.ev_tiles_end = ev_tiles_end
-    a.schedule, a.num_splits = int(schedule), int(num_splits)
-    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
-    if out_lse is not None:
-        if out_lse.dtype != torch.float32 or not out_lse.is_cuda or out_lse.numel() != B * Hq:
-            raise TypeError("out_lse must be an fp32 CUDA tensor with B*Hq entries")
-        a.out_lse = out_lse.data_ptr()
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
-    return out
+    return _keep[1]
 
 
 def attn_merge_shards(outs, lses, out=None, lse_out=None, stream=None):
@@ -237,6 +293,11 @@ def attn_merge_shards(outs, lses, out=None, lse_out=None, stream=None):
         raise ValueError("lses must be [S][rows] matching outs [S][rows][Hsz]")
     if out is None:
         out = torch.empty(outs.shape[1:], dtype=torch.float32, device=outs.device)
+    _f32_cuda("out", out, tuple(outs.shape[1:]))
+    if lse_out is not None:
+        _f32_cuda("lse_out", lse_out, tuple(lse_out.shape))
+        if lse_out.numel() != rows:
+            raise ValueError(f"lse_out must hold {rows} entries")
     _check(lib().attn_merge_shards(outs.data_ptr(), lses.data_ptr(), S, rows, Hsz, out.data_ptr(),
                                    None if lse_out is None else lse_out.data_ptr(), _stream_handle(stream)))
     return out
@@ -252,36 +313,11 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
                  schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, block_table=None,
-                 out_lse=None):
-        _bf16_cuda("q", q)
-        kv_dtype = _kv_cuda("k_cache", k_cache)
-        if _kv_cuda("v_cache", v_cache) != kv_dtype:
-            raise TypeError("k_cache and v_cache must have the same element type")
-        B, Hq, Hsz = q.shape
-        KH, S = k_cache.shape[1], k_cache.shape[2]
-        sl_ptr, on_dev, self._sl = _seqlens_arg(seqlens, B)
-        if v_cache.shape != k_cache.shape or k_cache.shape[3] != Hsz:
-            raise ValueError("k_cache/v_cache must share one shape ending in Hsz")
-        if block_table is None and k_cache.shape[0] != B:
-            raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
-        if tuple(out.shape) != (B, Hq, Hsz) or not out.is_cuda or not out.is_contiguous():
-            raise ValueError("out must be a contiguous fp32 CUDA tensor [B][Hq][Hsz]")
-        a = attn_decode_args()
-        a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-        a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
-        a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
-        a.kv_stride = 0 if block_table is not None else S
-        a.scale = float(scale)
-        a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
-        a.schedule, a.num_splits = int(schedule), int(num_splits)
-        a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
-        if block_table is not None:  # pools [num_blocks][KH][block_size][Hsz]
-            a.block_table = block_table.data_ptr()
-            a.block_size, a.max_blocks_per_seq, a.num_blocks = S, block_table.shape[1], k_cache.shape[0]
-            self._table = block_table
-        if out_lse is not None:  # fp32 [B][Hq] on the device
-            a.out_lse = out_lse.data_ptr()
-            self._lse = out_lse
+                 out_lse=None, workspace=None):
+        a, self._keep = _decode_args(q, k_cache, v_cache, seqlens, out, q_len=1, multi=False, paged=block_table is not None,
+                                     block_table=block_table, scale=scale, tile_keys=tile_keys,
+                                     num_ctas=num_ctas, schedule=schedule, num_splits=num_splits,
+                                     k_scale=k_scale, v_scale=v_scale, out_lse=out_lse, workspace=workspace)
         self._args = a
         self._ref = ctypes.byref(a)
         self._fn = lib().attn_decode_ex
@@ -358,33 +394,11 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seqlens, out=None, *, scal
     k_pool, v_pool: [num_blocks][KH][block_size][Hsz] (bf16 or FP8 E4M3 codes);
     block_table: int32 CUDA tensor [B][max_blocks_per_seq] of block ids.
     """
-    import torch
-    _bf16_cuda("q", q)
-    kv_dtype = _kv_cuda("k_pool", k_pool)
-    if _kv_cuda("v_pool", v_pool) != kv_dtype or v_pool.shape != k_pool.shape:
-        raise TypeError("k_pool and v_pool must have the same shape and element type")
-    if block_table.dtype != torch.int32 or not block_table.is_cuda or not block_table.is_contiguous():
-        raise TypeError("block_table must be a contiguous int32 CUDA tensor")
-    B, Hq, Hsz = q.shape
-    nblocks, KH, bs, Hsz2 = k_pool.shape
-    if Hsz2 != Hsz or block_table.dim() != 2 or block_table.shape[0] != B:
-        raise ValueError("pools must be [num_blocks][KH][block_size][Hsz], block_table [B][max_blocks]")
-    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
-    if out is None:
-        out = torch.empty((B, Hq, Hsz), dtype=torch.float32, device=q.device)
-    a = attn_decode_args()
-    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
-    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
-    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
-    a.kv_stride = 0
-    a.scale = float(scale)
-    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
-    a.schedule, a.num_splits = int(schedule), int(num_splits)
-    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
-    a.block_table = block_table.data_ptr()
-    a.block_size, a.max_blocks_per_seq, a.num_blocks = bs, block_table.shape[1], nblocks
+    a, keep = _decode_args(q, k_pool, v_pool, seqlens, out, q_len=1, multi=False, paged=True, block_table=block_table,
+                           scale=scale, tile_keys=tile_keys, num_ctas=num_ctas, schedule=schedule,
+                           num_splits=num_splits, k_scale=k_scale, v_scale=v_scale, out_lse=None, workspace=None)
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
-    return out
+    return keep[1]
 
 
 def attn_decode_multi_workspace_bytes(B: int, Hq: int, KH: int, Hsz: int, q_len: int, num_ctas: int = 0) -> int:
@@ -392,32 +406,17 @@ def attn_decode_multi_workspace_bytes(B: int, Hq: int, KH: int, Hsz: int, q_len:
 
 
 def attn_decode_multi(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_keys=0, num_ctas=0,
-                      schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, stream=None):
+                      schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, workspace=None,
+                      stream=None):
     """Multi-token decode (``attn_decode_ex`` with q_len = gamma): q [B][Hq][gamma][Hsz] bf16,
     caches [B][KH][S][Hsz] holding the drafted tokens last; query t attends keys
     0 .. L_b - gamma + t.  Returns out fp32 [B][Hq][gamma][Hsz]."""
-    import torch
-    _bf16_cuda("q", q)
-    kv_dtype = _kv_cuda("k_cache", k_cache)
-    if _kv_cuda("v_cache", v_cache) != kv_dtype:
-        raise TypeError("k_cache and v_cache must have the same element type")
-    B, Hq, gamma, Hsz = q.shape
-    KH, S = k_cache.shape[1], k_cache.shape[2]
-    sl_ptr, on_dev, _sl = _seqlens_arg(seqlens, B)
-    if k_cache.shape != (B, KH, S, Hsz) or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache/v_cache must be [B][KH][S][Hsz]")
-    if out is None:
-        out = torch.empty((B, Hq, gamma, Hsz), dtype=torch.float32, device=q.device)
-    a = attn_decode_args()
-    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
-    a.seqlens, a.seqlens_on_device, a.out = sl_ptr, on_dev, out.data_ptr()
-    a.B, a.Hq, a.KH, a.Hsz = B, Hq, KH, Hsz
-    a.kv_stride = S
-    a.scale = float(scale)
-    a.tile_keys, a.num_ctas = int(tile_keys), int(num_ctas)
-    a.schedule, a.num_splits = int(schedule), int(num_splits)
-    a.kv_dtype, a.k_scale, a.v_scale = kv_dtype, float(k_scale), float(v_scale)
-    a.q_len = gamma
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Hq][gamma][Hsz]")
+    a, keep = _decode_args(q, k_cache, v_cache, seqlens, out, q_len=q.shape[2], multi=True, paged=False, block_table=None,
+                           scale=scale, tile_keys=tile_keys, num_ctas=num_ctas, schedule=schedule,
+                           num_splits=num_splits, k_scale=k_scale, v_scale=v_scale, out_lse=None,
+                           workspace=workspace)
+    a.q_len = q.shape[2]
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
-    return out
-
+    return keep[1]

@@ -1,7 +1,9 @@
 // api.hip -- the C ABI (include/attn_gqa.h): validation, LeanTile planning, workspace, launches.
 //
-// Every argument check runs before the first HIP runtime call, so argument
-// errors are reported synchronously and leave no trace on the device.
+// Every argument check runs before anything is enqueued, so argument errors
+// are reported synchronously and leave no trace on the device.  Only the
+// checks that depend on the library's default workgroup count (a caller
+// workspace too small for it) come after a device query.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -15,7 +17,8 @@
 #include "../../include/attn_gqa.h"
 #include "common.h"
 
-static_assert(ATTN_MAX_GROUP == attn::kMaxGroup, "group limit mismatch");
+static_assert(ATTN_MAX_COLUMNS == attn::kMaxColumns, "column limit mismatch");
+static_assert(ATTN_MAX_COLUMN_ELEMS == attn::kMaxColumnElems, "column limit mismatch");
 static_assert(ATTN_MAX_CTAS == attn::kMaxCtas, "CTA limit mismatch");
 static_assert(ATTN_DECODE_COUNTER_BYTES == attn::kCounterBytes, "counter region mismatch");
 static_assert(ATTN_DECODE_PLAN_BYTES == attn::kPlanAreaBytes, "plan area mismatch");
@@ -47,14 +50,14 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;      // library-owned partial-state buffers
-std::map<std::pair<int, int>, int> g_default_ctas;          // (device, Hsz*64+G) -> resident CTAs
+std::map<std::pair<int, int>, int> g_default_ctas;          // (device, Hsz*1000+NC) -> resident CTAs
 
 int device_default_ctas(int Hsz, int G, int *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_pair(dev, Hsz * 64 + G);
+    auto key = std::make_pair(dev, Hsz * 1000 + G);
     auto it = g_default_ctas.find(key);
     if (it != g_default_ctas.end()) {
         *out = it->second;
@@ -119,7 +122,9 @@ int check_decode_dims(int B, int Hq, int KH, int Hsz) {
     if (B <= 0 || Hq <= 0 || KH <= 0) return fail(ATTN_ERR_SHAPE, "B, Hq and KH must be positive (B=%d Hq=%d KH=%d)", B, Hq, KH);
     if (Hq % KH != 0) return fail(ATTN_ERR_SHAPE, "Hq=%d is not a multiple of KH=%d", Hq, KH);
     if (Hsz != 64 && Hsz != 128 && Hsz != 256) return fail(ATTN_ERR_UNSUPPORTED, "Hsz=%d (supported: 64, 128, 256)", Hsz);
-    if (Hq / KH > attn::kMaxGroup) return fail(ATTN_ERR_UNSUPPORTED, "group size G=%d exceeds %d", Hq / KH, attn::kMaxGroup);
+    if (!attn::decode_columns_supported(Hq / KH, Hsz))
+        return fail(ATTN_ERR_UNSUPPORTED, "group size G=%d at Hsz=%d exceeds the column limit (G <= %d, G*Hsz <= %d)",
+                    Hq / KH, Hsz, attn::kMaxColumns, attn::kMaxColumnElems);
     if (B > ATTN_MAX_BATCH) return fail(ATTN_ERR_UNSUPPORTED, "B=%d exceeds %d", B, ATTN_MAX_BATCH);
     return ATTN_OK;
 }
@@ -212,12 +217,19 @@ const char *attn_last_error(void) { return g_last_error.c_str(); }
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int KH, int Hsz, int q_len, int num_ctas) {
     if (check_decode_dims(B, Hq, KH, Hsz) != ATTN_OK || num_ctas < 0 || q_len < 0) return 0;
     const int NC = (Hq / KH) * (q_len > 1 ? q_len : 1);
-    if (NC > attn::kMaxGroup) return 0;
+    if (!attn::decode_columns_supported(NC, Hsz)) return 0;
     int P = num_ctas;
     if (P == 0) {
+        // the larger of the two default counts: stream-K's, and the fixed split's
+        // B*KH*S with S = ceil(resident / (B*KH)) (capped so B*KH*S <= ATTN_MAX_CTAS),
+        // which only splits, and so only needs slots, when S >= 2
         int resident = 0;
         if (device_default_ctas(Hsz, NC, &resident) != ATTN_OK) return 0;
         P = stream_k_default_ctas((int64_t)B * KH, resident);
+        const int64_t segs = (int64_t)B * KH;
+        int64_t S = (resident + segs - 1) / segs;
+        if (S > attn::kMaxCtas / segs) S = attn::kMaxCtas / segs;
+        if (S >= 2 && segs * S > P) P = (int)(segs * S);
     }
     if (P > attn::kMaxCtas) return 0;
     return attn::decode_workspace_bytes(P, NC, Hsz);
@@ -227,8 +239,14 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas)
     return attn_decode_multi_workspace_bytes(B, Hq, KH, Hsz, 1, num_ctas);
 }
 
-int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
-    g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Where the partial-state workspace of a decode call comes from.
+enum class WorkspaceSource { Caller, Library };
+
+int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource src) {
     if (!a) return fail(ATTN_ERR_NULL, "args is NULL");
     if (!a->q || !a->k_cache || !a->v_cache || !a->seqlens || !a->out)
         return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, seqlens and out must be non-NULL");
@@ -241,8 +259,10 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (a->num_ctas > attn::kMaxCtas) return fail(ATTN_ERR_UNSUPPORTED, "num_ctas=%d exceeds %d", a->num_ctas, attn::kMaxCtas);
     if (a->q_len < 0) return fail(ATTN_ERR_SHAPE, "q_len=%d is negative", a->q_len);
     const int qlen = a->q_len > 1 ? a->q_len : 1;
-    if ((a->Hq / a->KH) * qlen > attn::kMaxGroup)
-        return fail(ATTN_ERR_UNSUPPORTED, "G*q_len=%d exceeds %d query columns", (a->Hq / a->KH) * qlen, attn::kMaxGroup);
+    if ((int64_t)(a->Hq / a->KH) * qlen > attn::kMaxColumns ||
+        !attn::decode_columns_supported((a->Hq / a->KH) * qlen, a->Hsz))
+        return fail(ATTN_ERR_UNSUPPORTED, "G*q_len=%lld query columns at Hsz=%d exceed the limit (<= %d, columns*Hsz <= %d)",
+                    (long long)(a->Hq / a->KH) * qlen, a->Hsz, attn::kMaxColumns, attn::kMaxColumnElems);
     const bool dev_sl = a->seqlens_on_device != 0;
     if (dev_sl) {
         if (((uintptr_t)a->seqlens & 3u) != 0) return fail(ATTN_ERR_ALIGN, "device seqlens must be 4-byte aligned");
@@ -292,7 +312,7 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     } else if (stride == 0) {
         for (int b = 0; b < a->B; ++b) stride = a->seqlens[b] > stride ? a->seqlens[b] : stride;
     }
-    const int T = a->tile_keys > 0 ? a->tile_keys : attn::decode_tile_keys(a->Hsz);
+    const int T = a->tile_keys > 0 ? a->tile_keys : attn::decode_tile_keys(a->Hsz, G * qlen);
 
     attn::DecodeParams p;
     if (dev_sl) {
@@ -336,15 +356,14 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     p.log2_block_size = log2_bs;
     p.num_blocks = a->num_blocks;
 
-    int P = a->num_ctas;
-    if (P > 0 && a->workspace && attn::decode_workspace_bytes(P, p.NC, a->Hsz) > a->workspace_bytes)
-        return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for num_ctas=%d", a->workspace_bytes,
-                    attn::decode_workspace_bytes(P, p.NC, a->Hsz), P);
-
-    // ---- argument checks done; HIP calls from here on ----
+    // ---- the schedule and the CTA count.  The device is queried only when
+    // the caller leaves the count to the library, so that with an explicit
+    // stream-K count every argument error (the workspace size included) is
+    // still reported before the first HIP call. ----
     int resident = 0;
-    st = device_default_ctas(a->Hsz, p.NC, &resident);
-    if (st != ATTN_OK) return st;
+    auto query_resident = [&]() -> int {
+        return resident > 0 ? ATTN_OK : device_default_ctas(a->Hsz, p.NC, &resident);
+    };
     // The selector (the digest's runtime selection policy: stream-K tiles for
     // long, few-head or ragged work; no split when the batch alone fills every
     // resident slot evenly) runs one CTA per segment when that finishes no later
@@ -352,10 +371,12 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     // states at all), and stream-K otherwise.  With device seqlens the host
     // cannot see the lengths, and stream-K is the choice that never leaves a
     // long context to one CTA.
+    int P = a->num_ctas;
     int schedule = a->schedule;
     if (schedule == ATTN_SCHEDULE_AUTO) {
         schedule = ATTN_SCHEDULE_STREAM_K;
         if (!dev_sl && a->num_ctas == 0 && p.plan.N > 0) {
+            if ((st = query_resident()) != ATTN_OK) return st;
             std::vector<int64_t> heap((size_t)resident);
             const int64_t even = (p.plan.N + resident - 1) / resident;
             if (plan_whole_segments_makespan(p.plan, resident, heap.data()) <= even)
@@ -363,13 +384,23 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         }
     }
     if (schedule == ATTN_SCHEDULE_FIXED_SPLIT) {
-        const int S = a->num_splits > 0 ? a->num_splits
-                      : a->schedule == ATTN_SCHEDULE_AUTO ? 1 : default_splits(p.plan, resident);
+        int S = a->num_splits;
+        if (S == 0) {
+            if (a->schedule == ATTN_SCHEDULE_AUTO) {
+                S = 1;
+            } else {
+                if ((st = query_resident()) != ATTN_OK) return st;
+                S = default_splits(p.plan, resident);
+            }
+        }
         p.plan.mode = kPlanFixedSplit;
         p.plan.splits = S;
         P = a->B * a->KH * S;
     } else {
-        if (P == 0) P = stream_k_default_ctas((int64_t)a->B * a->KH, resident);
+        if (P == 0) {
+            if ((st = query_resident()) != ATTN_OK) return st;
+            P = stream_k_default_ctas((int64_t)a->B * a->KH, resident);
+        }
         // no empty CTA; one CTA zeroes an all-empty batch (with device seqlens the device clamps P)
         if (!dev_sl && P > p.plan.N) P = p.plan.N > 0 ? (int)p.plan.N : 1;
     }
@@ -384,17 +415,18 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     if (!dev_sl && p.plan.N > 0 && !scan_segments(p.plan, &split, &wide))
         return fail(ATTN_ERR_UNSUPPORTED, "more than %d heads split over more than %d workgroups", attn::kMaxWideHeads,
                     attn::kMergeFanIn);
+    const size_t need = split ? attn::decode_workspace_bytes(P, p.NC, a->Hsz) : 0;
+    if (split && src == WorkspaceSource::Caller && a->workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for %d workgroups", a->workspace_bytes, need, P);
+
+    // ---- HIP calls from here on ----
     if (split) {
-        const size_t need = attn::decode_workspace_bytes(P, p.NC, a->Hsz);
         char *w = nullptr;
-        if (a->workspace) {
-            if (a->workspace_bytes < need)
-                return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed", a->workspace_bytes, need);
+        if (src == WorkspaceSource::Caller) {
             w = static_cast<char *>(a->workspace);
         } else {
             void *lw = nullptr;
-            st = library_workspace(stream, need, &lw);
-            if (st != ATTN_OK) return st;
+            if ((st = library_workspace(stream, need, &lw)) != ATTN_OK) return st;
             w = static_cast<char *>(lw);
         }
         p.counters = reinterpret_cast<int *>(w);
@@ -422,13 +454,12 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         most = most < segs ? most : segs;
         wide.count = (int)(most < attn::kMaxWideHeads ? most : attn::kMaxWideHeads);
     }
-    if (a->ev_tiles_begin && (e = hipEventRecord(a->ev_tiles_begin, stream)) != hipSuccess)
-        return fail_hip(e, "hipEventRecord(begin)");
-    e = attn::launch_decode_tiles(p, a->Hsz, fp8, stream);
+    // The timing events are bound to the start of the tile kernel and to the end
+    // of the last decode kernel of the call.
+    const bool merge_follows = p.ws && wide.count > 0;
+    e = attn::launch_decode_tiles(p, a->Hsz, fp8, stream, a->ev_tiles_begin, merge_follows ? nullptr : a->ev_tiles_end);
     if (e != hipSuccess) return fail_hip(e, "decode tile kernel launch");
-    if (a->ev_tiles_end && (e = hipEventRecord(a->ev_tiles_end, stream)) != hipSuccess)
-        return fail_hip(e, "hipEventRecord(end)");
-    if (p.ws && wide.count > 0) {
+    if (merge_follows) {
         wide.ws = p.ws;
         wide.out = p.out;
         wide.lse = p.lse;
@@ -438,10 +469,20 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
         wide.Hq = p.Hq;
         wide.qlen = p.qlen;
         wide.v_scale = p.v_scale;
-        e = attn::launch_merge_wide(wide, a->Hsz, stream);
+        e = attn::launch_merge_wide(wide, a->Hsz, stream, a->ev_tiles_end);
         if (e != hipSuccess) return fail_hip(e, "wide merge kernel launch");
     }
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
+    g_last_error.clear();
+    if (a && a->workspace) return decode_impl(a, stream, WorkspaceSource::Caller);
+    return decode_impl(a, stream, WorkspaceSource::Library);
 }
 
 int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out, float *lse_out,

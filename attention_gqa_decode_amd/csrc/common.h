@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "plan.h"
 
 namespace attn {
@@ -14,8 +16,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxGroup = 16;       // query heads per kv head held by one workgroup (MFMA N = 16)
-constexpr int kKeysPerBlock = 32;   // keys one wave consumes per step (two 16-key MFMA row blocks)
+// Query columns one decode workgroup holds: G query heads x q_len drafted
+// tokens, in blocks of 16 MFMA columns.  At most kMaxColumns of them, and
+// columns x Hsz at most kMaxColumnElems (their output accumulators live in
+// registers: 64 columns at Hsz 64 or 128, 32 at Hsz 256).
+constexpr int kMaxColumns = 64;
+constexpr int kMaxColumnElems = 64 * 128;
+inline bool decode_columns_supported(int NC, int Hsz) {
+    return NC >= 1 && NC <= kMaxColumns && NC * Hsz <= kMaxColumnElems;
+}
 
 // Kernel arguments of the decode tile kernel (passed by value: the plan rides in kernargs).
 struct DecodeParams {
@@ -87,9 +96,17 @@ inline size_t decode_workspace_bytes(int P, int NC, int Hsz) {
     return kCounterBytes + kPlanAreaBytes + (size_t)2 * P * decode_slot_floats(NC, Hsz) * sizeof(float);
 }
 
+// Raises `fn`'s dynamic-LDS limit to `lds` bytes on the current device if it is
+// above the 64 KiB default; `done` is a kMaxLdsDevices-entry record of the
+// largest size already set per device (zero-initialised, one per kernel).
+constexpr int kMaxLdsDevices = 64;
+hipError_t ensure_lds_limit(const void *fn, std::atomic<int> *done, size_t lds);
+
 // Launchers (return hipError_t of the launch).
-hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream);
-hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream);
+// Optional timing events are bound to the kernels' own start and end timestamps.
+hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream,
+                               hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream, hipEvent_t ev_end = nullptr);
 // Builds the LeanPlan of `base` (B, KH, T, mode, splits, P) for the device
 // seqlens on the device, clamping each L_b into [0, stride], and lists the wide
 // heads; one workgroup.
@@ -102,7 +119,7 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out,
                                float *lse_out, hipStream_t stream);
 int decode_tiles_occupancy(int Hsz, int NC);  // resident decode workgroups per CU
-int decode_tile_keys(int Hsz);               // default LeanTile: one 32-key block per wave
+int decode_tile_keys(int Hsz, int NC);       // default LeanTile: one block per wave
 hipError_t launch_prefill_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                                  int B, int ISL, int Hq, int KH, int Hsz, float scale_log2,
                                  hipStream_t stream);

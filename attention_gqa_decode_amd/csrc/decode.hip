@@ -45,12 +45,12 @@
 //  ever waits for another, so neither merge needs co-residency.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 #include <atomic>
 
 namespace attn {
 namespace {
-
-constexpr int kMaxDevices = 64;
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -83,16 +83,24 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-// Waves per workgroup: 8 while a wave's 32-key K/V staging fits (LDS), 4 at Hsz = 256.
-template <int HSZ>
+// Launch shape for head dimension HSZ and NCB blocks of 16 MFMA columns (the
+// query columns: G heads x q_len drafted tokens, up to 16 NCB of them).
+//  * KPB keys per wave block: 32, or 16 at HSZ = 256 (so one block is 16 KiB
+//    of bf16 K+V at every head dimension and its staging takes 64 registers
+//    per lane) and with 64 columns at HSZ = 128 (whose accumulators leave no
+//    room for more).
+//  * W waves per workgroup: 8 (two per SIMD, 256 registers each) where the
+//    wave fits, else 4 (one per SIMD, up to 512 registers with the AGPRs).
+template <int HSZ, int NCB>
 struct DecodeCfg {
-    static constexpr int W = HSZ == 256 ? 4 : 8;
+    static constexpr int KPB = HSZ == 256 || HSZ * NCB >= 512 ? 16 : 32;
+    static constexpr int KB = KPB / 16;                  // 16-key MFMA row blocks per wave block
+    static constexpr int W = NCB == 1 ? 8 : (NCB == 2 && HSZ == 64 ? 8 : 4);
+    static constexpr int NCMAX = 16 * NCB;               // MFMA columns
     static constexpr int NS = HSZ / 32;                  // MFMA K steps over d
     static constexpr int ND = HSZ / 16;                  // 16-wide d blocks of the output
-    static constexpr int CH = HSZ / 8;                   // 16-byte chunks per row
     static constexpr int RS = HSZ + 8;                   // staged row stride (bf16), 16 B pad
-    static constexpr int LOADS = 2 * kKeysPerBlock * CH / 64;  // 16-byte loads per lane per block (K + V)
-    static constexpr int STAGE = 2 * kKeysPerBlock * RS;       // bf16 per wave: K rows then V rows
+    static constexpr int STAGE = 2 * KPB * RS;           // bf16 per wave: K rows then V rows
 };
 
 // One wave's next block in registers: fully coalesced 16-byte loads (lane l of
@@ -100,16 +108,17 @@ struct DecodeCfg {
 // non-temporal because every byte is used exactly once.  Rows past klast are
 // clamped re-reads of row klast (their scores are masked later).  An element
 // is 2 bytes (bf16) or 1 byte (FP8 E4M3): a 16-byte chunk holds 8 or 16 of them.
-template <int HSZ, bool FP8>
+template <int HSZ, bool FP8, int KPB>
 struct KvCfg {
     static constexpr int EPC = FP8 ? 16 : 8;                          // elements per 16-byte chunk
     static constexpr int CPR = HSZ / EPC;                             // chunks per row
-    static constexpr int LOADS = 2 * kKeysPerBlock * CPR / 64;        // chunks per lane per block (K + V)
+    static constexpr int LOADS = 2 * KPB * CPR / 64;                  // chunks per lane per block (K + V)
+    static_assert(KPB * CPR % 64 == 0, "a block's chunks split evenly over the lanes");
 };
 
-template <int HSZ, bool FP8>
+template <int HSZ, bool FP8, int KPB>
 struct Staged {
-    u32x4 r[KvCfg<HSZ, FP8>::LOADS];
+    u32x4 r[KvCfg<HSZ, FP8, KPB>::LOADS];
 };
 
 // Where the rows of one (request, kv head) context live.  Contiguous: row j of
@@ -133,10 +142,10 @@ struct KvRows {
     }
 };
 
-template <int HSZ, bool FP8, bool PAGED>
-__device__ __forceinline__ void load_block(Staged<HSZ, FP8> &st, const KvRows<PAGED> &kv, int key0, int klast,
+template <int HSZ, bool FP8, bool PAGED, int KPB>
+__device__ __forceinline__ void load_block(Staged<HSZ, FP8, KPB> &st, const KvRows<PAGED> &kv, int key0, int klast,
                                            int lane) {
-    using K = KvCfg<HSZ, FP8>;
+    using K = KvCfg<HSZ, FP8, KPB>;
     constexpr int HALF = K::LOADS / 2;
     constexpr int EB = FP8 ? 1 : 2;  // bytes per element
 #pragma unroll
@@ -169,17 +178,17 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4 &w, u32x4 &lo, u32x4 
 
 // Registers -> this wave's LDS stage as bf16, rows padded by 16 bytes
 // (row-parallel 16-byte reads of the MFMA operands then hit distinct banks).
-template <int HSZ, bool FP8>
-__device__ __forceinline__ void store_block(const Staged<HSZ, FP8> &st, uint16_t *stage, int lane) {
-    using C = DecodeCfg<HSZ>;
-    using K = KvCfg<HSZ, FP8>;
+template <int HSZ, bool FP8, int KPB>
+__device__ __forceinline__ void store_block(const Staged<HSZ, FP8, KPB> &st, uint16_t *stage, int lane) {
+    constexpr int RS = HSZ + 8;
+    using K = KvCfg<HSZ, FP8, KPB>;
     constexpr int HALF = K::LOADS / 2;
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
         const int c = 64 * j + lane;
         const int row = c / K::CPR, col = K::EPC * (c % K::CPR);
-        uint16_t *kd = stage + row * C::RS + col;
-        uint16_t *vd = stage + (kKeysPerBlock + row) * C::RS + col;
+        uint16_t *kd = stage + row * RS + col;
+        uint16_t *vd = stage + (KPB + row) * RS + col;
         if constexpr (FP8) {
             u32x4 a, b;
             fp8x16_to_bf16(st.r[j], a, b);
@@ -197,81 +206,115 @@ __device__ __forceinline__ void store_block(const Staged<HSZ, FP8> &st, uint16_t
 
 __device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-// BMM1 -> online softmax -> BMM2 for one staged 32-key block of one wave; keys
-// after kmax (the piece's end, or the causal limit of the lane's drafted token)
-// are masked.
-template <int HSZ>
-__device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[HSZ / 32],
-                                              int key0, int kmax, int col, int grp,
-                                              float scale_log2, float &m_run, float &l_run,
-                                              f32x4 (&oacc)[HSZ / 16]) {
-    using C = DecodeCfg<HSZ>;
+// BMM1 -> online softmax -> BMM2 for one staged block of KPB keys of one wave.
+// Column block cb holds MFMA columns 16 cb .. 16 cb + 15; in every lane
+// (col, grp) its keys after kmax[cb] (the piece's end, or the causal limit of
+// the lane's drafted token) are masked.  Each K and V operand read from LDS
+// serves all NCB column blocks.
+template <int HSZ, int NCB>
+__device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[NCB][HSZ / 32],
+                                              int key0, const int (&kmax)[NCB], int col, int grp,
+                                              float scale_log2, float (&m_run)[NCB], float (&l_run)[NCB],
+                                              f32x4 (&oacc)[NCB][HSZ / 16]) {
+    using C = DecodeCfg<HSZ, NCB>;
     constexpr int NS = C::NS;
     constexpr int ND = C::ND;
+    constexpr int KB = C::KB;
     const float NEG_INF = -__builtin_inff();
-    const uint16_t *krow = stage + col * C::RS + 8 * grp;                        // key col of 16-key block 0
-    // BMM1: S^T[key][g] for keys key0 + 16kb + 4grp + i in lane (g = col, grp)
-    f32x4 sc[2];
+    const uint16_t *krow = stage + col * C::RS + 8 * grp;  // key col of 16-key row block 0
+    // BMM1: S^T[key][c] for keys key0 + 16kb + 4grp + i in lane (c = 16cb + col, grp)
+    f32x4 sc[NCB][KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) sc[kb] = mfma_bf16(lds_row8(krow + 16 * kb * C::RS + 32 * s), qop[s], sc[kb]);
-    }
-    float x[8];
-    float mx = NEG_INF;
+        for (int kb = 0; kb < KB; ++kb) sc[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * kb + 4 * grp + i;
-            const float xv = key <= kmax ? sc[kb][i] * scale_log2 : NEG_INF;
-            x[4 * kb + i] = xv;
-            mx = fmaxf(mx, xv);
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 a = lds_row8(krow + 16 * kb * C::RS + 32 * s);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) sc[cb][kb] = mfma_bf16(a, qop[cb][s], sc[cb][kb]);
         }
-    mx = wave_max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    // -inf only while a drafted token's column has seen no key yet (its limit lies before this block)
-    const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ps = 0.f;
-    bf16x8 phi, plo;
+    // online softmax per column block; P enters BMM2 as its bf16 hi and lo parts
+    bf16x8 phi[NCB], plo[NCB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(x[i] - m_use);
-        ps += pv;
-        const __bf16 hi = (__bf16)pv;
-        phi[i] = hi;
-        plo[i] = (__bf16)(pv - (float)hi);
+    for (int cb = 0; cb < NCB; ++cb) {
+        float x[4 * KB];
+        float mx = NEG_INF;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + 16 * kb + 4 * grp + i;
+                const float xv = key <= kmax[cb] ? sc[cb][kb][i] * scale_log2 : NEG_INF;
+                x[4 * kb + i] = xv;
+                mx = fmaxf(mx, xv);
+            }
+        mx = wave_max_over_groups(mx);
+        const float m_new = fmaxf(m_run[cb], mx);
+        // -inf only while a drafted token's column has seen no key yet (its limit lies before this block)
+        const float m_use = m_new == NEG_INF ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4 * KB; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(x[i] - m_use);
+            ps += pv;
+            const __bf16 hi = (__bf16)pv;
+            phi[cb][i] = hi;
+            plo[cb][i] = (__bf16)(pv - (float)hi);
+        }
+        l_run[cb] = l_run[cb] * alpha + ps;
+        m_run[cb] = m_new;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[cb][db] *= alpha;
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-    // BMM2: the Vᵀ operand comes straight out of the row-major V stage through
-    // transposing reads.  Lane (i, grp) gets V[4 grp + j][16 db + i] and
-    // V[16 + 4 grp + j][16 db + i], j = 0..3: the key order of this lane's Sᵀ
-    // accumulator, so P needs no shuffle.  P enters as its bf16 hi and lo parts.
-    const uint16_t *vstage = stage + kKeysPerBlock * C::RS;
+    // BMM2: the V^T operand comes straight out of the row-major V stage through
+    // transposing reads.  Lane (i, grp) gets V[4 grp + j][16 db + i] (and, with
+    // 32-key blocks, V[16 + 4 grp + j][16 db + i]), j = 0..3: the key order of
+    // this lane's S^T accumulator, so P needs no shuffle.
+    const uint16_t *vstage = stage + C::KPB * C::RS;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
         const i16x4 a = v_cols(vstage, C::RS, 4 * grp, 16 * db, col);
-        const i16x4 b = v_cols(vstage, C::RS, 16 + 4 * grp, 16 * db, col);
-        const bf16x8 vt = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma_bf16(vt, phi, oacc[db]);
-        oacc[db] = mfma_bf16(vt, plo, oacc[db]);
+        if constexpr (KB == 2) {
+            const i16x4 b = v_cols(vstage, C::RS, 16 + 4 * grp, 16 * db, col);
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                oacc[cb][db] = mfma_bf16(vt, phi[cb], oacc[cb][db]);
+                oacc[cb][db] = mfma_bf16(vt, plo[cb], oacc[cb][db]);
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const i16x4 ph = __builtin_bit_cast(i16x4, bf16x4{phi[cb][0], phi[cb][1], phi[cb][2], phi[cb][3]});
+                const i16x4 pl = __builtin_bit_cast(i16x4, bf16x4{plo[cb][0], plo[cb][1], plo[cb][2], plo[cb][3]});
+                oacc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, oacc[cb][db], 0, 0, 0);
+                oacc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, oacc[cb][db], 0, 0, 0);
+            }
+        }
     }
 }
 
 // Partial slots and merge counters are shared between CTAs that may sit on
 // different XCDs, whose L2 caches are not coherent with each other.  Every
-// access to a slot therefore goes through agent-scope atomic loads and stores
-// (relaxed order), which the memory system keeps coherent per location without
-// any L2 writeback or invalidate; a writer waits for its stores to complete
-// (s_waitcnt) before it arrives at the counter, and a reader issues its loads
-// only after its arrival returned.  Agent-scope fences would also be correct,
-// but each one writes back and invalidates a whole L2 and measured several
-// times slower on MI355X.
+// access to a slot goes through agent-scope atomic loads and stores (relaxed
+// order): on gfx950 these carry device scope in the instruction (sc1), so a
+// store is written through to the device-wide coherence point and a load
+// reads from it, bypassing the XCD's L2; no L2 writeback or invalidate is
+// involved.  Every writing wave waits for its slot stores to be acknowledged
+// (s_waitcnt vmcnt(0), after which they are performed at that point) before
+// the workgroup barrier; one thread then arrives at the head's counter with a
+// device-scope atomic add, which is issued after the barrier and so after
+// every acknowledged slot store of the workgroup.  The CTA that sees the last
+// arrival issues its slot loads only after that atomic returned.  The order is
+// therefore enforced by the instruction stream and the device-scope accesses
+// themselves.  An acquire-release add (an L2 writeback before the arrival and
+// an L2 invalidate after it, the HIP memory model's formal route) measured
+// 3.5% slower on the Llama-3-8B-shaped batch and 11% slower on the ragged
+// batch with one query head per kv head, so it is not used.
 // (Whole-vector bit casts only: a bit cast of a single vector element is not
 // reliable with this compiler.)
 __device__ __forceinline__ void st_shared_f4(float *p, const f32x4 &v) {
@@ -314,7 +357,7 @@ __device__ __forceinline__ int partial_slot(const LeanPlan &pl, int c_lo, int64_
 // them to their common max and writes the output.  Wider heads are left to
 // merge_wide_kernel, which reads their partials with many workgroups at once.
 // All control flow is uniform over the CTA.
-template <int HSZ, int NT>
+template <int HSZ, int NT, int NCMAX>
 __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPiece &pc, int *flag) {
     const int NC = p.NC, G = p.G;
     const int tid = threadIdx.x;
@@ -324,19 +367,15 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
     __syncthreads();  // every wave's slot stores have completed
     if (tid == 0) {
         int *cnt = p.counters + partial_slot(pl, c_lo, pc.seg_begin, 0);
-        const int old = atomicAdd(cnt, 1);
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = old == n - 1;
         if (last) atomicExch(cnt, 0);  // counters are zero again for the next call
         *flag = last;
     }
     __syncthreads();
     if (!*flag) return;
-    constexpr int UNITS = kMaxGroup * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound (NC <= 16)
     const int units = NC * HSZ / 4;
-#pragma unroll
-    for (int r = 0; r < UNITS; ++r) {
-        const int u = tid + r * NT;
-        if (u >= units) continue;
+    auto merge_unit = [&](int u) {
         const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
         float mv[kMergeFanIn], lv[kMergeFanIn];
         f32x4 ov[kMergeFanIn];
@@ -369,6 +408,16 @@ __device__ void merge_up(const DecodeParams &p, const LeanPlan &pl, const LeanPi
         const int64_t orow = ((int64_t)pc.b * p.Hq + pc.kh * G + g % G) * p.qlen + g / G;
         *reinterpret_cast<f32x4 *>(p.out + orow * HSZ + 4 * d4) = O * (p.v_scale / L);
         if (p.lse && d4 == 0) p.lse[orow] = M + __log2f(L);
+    };
+    // A short loop is unrolled (its loads then overlap); a long one, with 32 or
+    // more columns, runs as a loop so its registers stay within the kernel's budget.
+    constexpr int UNITS = NCMAX * HSZ / 4 / NT + 1;  // float4 outputs per thread, upper bound
+    if constexpr (UNITS <= 3) {
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r)
+            if (tid + r * NT < units) merge_unit(tid + r * NT);
+    } else {
+        for (int u = tid; u < units; u += NT) merge_unit(u);
     }
 }
 
@@ -574,27 +623,43 @@ __device__ __forceinline__ LeanPiece uniform_piece(const LeanPiece &x) {
     return u;
 }
 
+template <int KPB>
 __device__ __forceinline__ int piece_blocks(const LeanPiece &pc) {
-    return (pc.key_end - pc.key_begin + kKeysPerBlock - 1) / kKeysPerBlock;
+    return (pc.key_end - pc.key_begin + KPB - 1) / KPB;
 }
 
-template <int HSZ, bool FP8, bool PAGED>
-__global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(const DecodeParams p) {
-    using C = DecodeCfg<HSZ>;
+// The waves of a CTA take the blocks of a piece in any order (the softmax merge
+// is order-free), so each CTA starts its walk at its own rotation of the piece:
+// block i of the walk is block (i + rot) mod nblk.  CTA ranges of equal-length
+// contexts sit at power-of-two strides, and without the rotation every CTA
+// would read the same offset of its range, hence the same HBM channels, at the
+// same moment.
+__device__ __forceinline__ int piece_rotation(int c, int nblk) { return (int)(((unsigned)c * 13u) % (unsigned)nblk); }
+
+__device__ __forceinline__ int rotated_block(int i, int rot, int nblk) {
+    const int j = i + rot;
+    return j < nblk ? j : j - nblk;
+}
+
+template <int HSZ, bool FP8, bool PAGED, int NCB>
+__global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_kernel(const DecodeParams p) {
+    using C = DecodeCfg<HSZ, NCB>;
     constexpr int NS = C::NS;
     constexpr int ND = C::ND;
     constexpr int W = C::W;
+    constexpr int KPB = C::KPB;
+    constexpr int NCMAX = C::NCMAX;
     constexpr int OSTRIDE = HSZ + 4;  // padded LDS row of the cross-wave reduction
     extern __shared__ __attribute__((aligned(16))) float smem[];
     // streaming phase: one K/V stage per wave; piece epilogue: the reduction buffers
     uint16_t *stages = reinterpret_cast<uint16_t *>(smem);
-    float *sm_m = smem;               // [W][16]
-    float *sm_l = smem + W * 16;      // [W][16]
-    float *sm_o = smem + 2 * W * 16;  // [W][NC][OSTRIDE]
+    float *sm_m = smem;                  // [W][NCMAX]
+    float *sm_l = smem + W * NCMAX;      // [W][NCMAX]
+    float *sm_o = smem + 2 * W * NCMAX;  // [W][NC][OSTRIDE]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: block indices stay scalar
-    const int col = lane & 15;  // head g (Q, P, O), key row (K, V) or d (V^T)
+    const int col = lane & 15;  // column within a 16-column block (Q, P, O), key row (K, V) or d (V^T)
     const int grp = lane >> 4;  // 8-wide slice of the MFMA contraction
     const int c = blockIdx.x;
     const int G = p.G, NC = p.NC;
@@ -602,7 +667,7 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     uint16_t *stage = stages + wave * C::STAGE;
 
     __shared__ int merge_flag;
-    __shared__ int blk_next;  // next unclaimed 32-key block of the current piece
+    __shared__ int blk_next;  // next unclaimed block of the current piece
     // The plan is read many times (piece lookups, merge slots): one copy in LDS
     // costs a single round of vector loads instead of chains of dependent
     // scalar loads from the argument segment.
@@ -628,13 +693,15 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
     // every wave's start-up instructions then run while they are in flight.
     int64_t t = plan_cta_begin(pl, c);
     const int64_t t_end = plan_cta_begin(pl, c + 1);
-    Staged<HSZ, FP8> st;
+    Staged<HSZ, FP8, KPB> st;
     LeanPiece pc0 = {};
     if (t < t_end) {
         pc0 = uniform_piece(plan_piece_at(pl, t, t_end));
-        if (wave < piece_blocks(pc0))
-            load_block<HSZ, FP8, PAGED>(st, piece_rows<HSZ, FP8, PAGED>(p, pl, pc0.b, pc0.kh),
-                                        pc0.key_begin + wave * kKeysPerBlock, pc0.key_end - 1, lane);
+        const int nblk0 = piece_blocks<KPB>(pc0);
+        if (wave < nblk0)
+            load_block<HSZ, FP8, PAGED, KPB>(st, piece_rows<HSZ, FP8, PAGED>(p, pl, pc0.b, pc0.kh),
+                                             pc0.key_begin + rotated_block(wave, piece_rotation(c, nblk0), nblk0) * KPB,
+                                             pc0.key_end - 1, lane);
     }
 
     // Requests with an empty context own no tiles: their output rows are zero.
@@ -653,27 +720,33 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         const KvRows<PAGED> kv = piece_rows<HSZ, FP8, PAGED>(p, pl, pc.b, pc.kh);
         const int h0 = pc.kh * G;
 
-        bf16x8 qop[NS];
-        // column col holds query token col / G of head h0 + col % G (q is [B][Hq][qlen][Hsz])
-        const int ccol = col < NC ? col : 0;
-        const uint16_t *qrow = p.q + (((int64_t)pc.b * p.Hq + h0 + ccol % G) * p.qlen + ccol / G) * HSZ;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            bf16x8 z = {};
-            qop[s] = col < NC ? load_row8(qrow + 32 * s + 8 * grp) : z;
-        }
-
-        float m_run = NEG_INF;  // running max (log2 domain) of head `col`
-        float l_run = 0.f;      // this lane's share of the running sum
-        f32x4 oacc[ND];         // O[col][16*db + 4*grp + i]
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        const int nblk = piece_blocks(pc);
+        // Column c = 16 cb + col holds query token c / G of head h0 + c % G (q is
+        // [B][Hq][qlen][Hsz]); columns past NC are zero.
+        bf16x8 qop[NCB][NS];
+        float m_run[NCB];  // running max (log2 domain) of column c
+        float l_run[NCB];  // this lane's share of the running sum
+        f32x4 oacc[NCB][ND];  // O[c][16*db + 4*grp + i]
+        int kmax[NCB];
+        const int nblk = piece_blocks<KPB>(pc);
         const int klast = pc.key_end - 1;
-        // drafted token t (column col) sees keys up to L_b - qlen + t
-        const int climit = pl.seqlen[pc.b] - p.qlen + ccol / G;
-        const int kmax = klast < climit ? klast : climit;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int cc = 16 * cb + col;
+            const int ccol = cc < NC ? cc : 0;
+            const uint16_t *qrow = p.q + (((int64_t)pc.b * p.Hq + h0 + ccol % G) * p.qlen + ccol / G) * HSZ;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 z = {};
+                qop[cb][s] = cc < NC ? load_row8(qrow + 32 * s + 8 * grp) : z;
+            }
+            m_run[cb] = NEG_INF;
+            l_run[cb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) oacc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // drafted token t sees keys up to L_b - qlen + t
+            const int climit = pl.seqlen[pc.b] - p.qlen + ccol / G;
+            kmax[cb] = klast < climit ? klast : climit;
+        }
         // Block w starts on wave w; every wave claims its next block from an
         // LDS counter when it starts computing one, so waves whose loads come
         // back sooner take more blocks and all waves of the CTA finish within
@@ -681,19 +754,22 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
         int blk = wave;
-        if (!first_piece && blk < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + blk * kKeysPerBlock, klast, lane);
+        const int rot = piece_rotation(c, nblk);
+        if (!first_piece && blk < nblk)
+            load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + rotated_block(blk, rot, nblk) * KPB, klast, lane);
         first_piece = false;
         while (blk < nblk) {
-            store_block<HSZ, FP8>(st, stage, lane);
+            store_block<HSZ, FP8, KPB>(st, stage, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             int nxt = 0;
             if (lane == 0) nxt = atomicAdd(&blk_next, 1);
             nxt = __builtin_amdgcn_readfirstlane(nxt);
-            if (nxt < nblk) load_block<HSZ, FP8, PAGED>(st, kv, pc.key_begin + nxt * kKeysPerBlock, klast, lane);
+            if (nxt < nblk)
+                load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + rotated_block(nxt, rot, nblk) * KPB, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ>(stage, qop, pc.key_begin + blk * kKeysPerBlock, kmax, col, grp, p.scale_log2,
-                               m_run, l_run, oacc);
+            process_block<HSZ, NCB>(stage, qop, pc.key_begin + rotated_block(blk, rot, nblk) * KPB, kmax, col, grp,
+                                    p.scale_log2, m_run, l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             blk = nxt;
@@ -704,39 +780,40 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
         // merges one float4 column of the piece's NC x HSZ state over the W
         // waves (rescale to the common max, sum) and stores it straight to the
         // output or to the partial slot.
-        l_run = wave_sum_over_groups(l_run);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) l_run[cb] = wave_sum_over_groups(l_run[cb]);
         __syncthreads();  // every wave left the streaming loop: stages and block counter are free
         if (threadIdx.x == 0) blk_next = W;  // for the next piece (later barriers publish it)
-        if (grp == 0) {
-            sm_m[wave * 16 + col] = m_run;
-            sm_l[wave * 16 + col] = l_run;
-        }
-        if (col < NC) {
-            float *dst = sm_o + (wave * NC + col) * OSTRIDE + 4 * grp;
 #pragma unroll
-            for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[db];
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int cc = 16 * cb + col;
+            if (grp == 0) {
+                sm_m[wave * NCMAX + cc] = m_run[cb];
+                sm_l[wave * NCMAX + cc] = l_run[cb];
+            }
+            if (cc < NC) {
+                float *dst = sm_o + (wave * NC + cc) * OSTRIDE + 4 * grp;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) *reinterpret_cast<f32x4 *>(dst + 16 * db) = oacc[cb][db];
+            }
         }
         __syncthreads();
 
         const bool whole = pc.tile_begin == pc.seg_begin && pc.tile_end == pc.seg_end;
         const int64_t so = whole ? 0 : (int64_t)plan_slot(pl, c, pc.seg_begin) * p.slot_floats;
-        constexpr int UNITS = (kMaxGroup * HSZ / 4 + W * 64 - 1) / (W * 64);  // float4 columns per thread, at most
         const int units = NC * HSZ / 4;
-#pragma unroll
-        for (int r = 0; r < UNITS; ++r) {
-            const int u = threadIdx.x + r * W * 64;
-            if (u >= units) continue;
+        auto reduce_unit = [&](int u) {
             const int g = u / (HSZ / 4), d4 = u % (HSZ / 4);
             float M = NEG_INF;
 #pragma unroll
-            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * NCMAX + g]);
             float Lt = 0.f;
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                const float mw = sm_m[w * 16 + g];
+                const float mw = sm_m[w * NCMAX + g];
                 const float f = mw == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-                Lt += sm_l[w * 16 + g] * f;
+                Lt += sm_l[w * NCMAX + g] * f;
                 O += *reinterpret_cast<const f32x4 *>(sm_o + (w * NC + g) * OSTRIDE + 4 * d4) * f;
             }
             if (whole) {
@@ -751,40 +828,133 @@ __global__ __launch_bounds__(DecodeCfg<HSZ>::W * 64) void decode_tiles_kernel(co
                     st_shared_f(p.ws + so + NC * HSZ + NC + g, Lt);
                 }
             }
+        };
+        constexpr int UNITS = (NCMAX * HSZ / 4 + W * 64 - 1) / (W * 64);  // float4 columns per thread, at most
+        if constexpr (UNITS <= 2) {
+#pragma unroll
+            for (int r = 0; r < UNITS; ++r)
+                if ((int)threadIdx.x + r * W * 64 < units) reduce_unit(threadIdx.x + r * W * 64);
+        } else {
+            for (int u = threadIdx.x; u < units; u += W * 64) reduce_unit(u);
         }
         if (!whole) wait_memory();
-        if (!whole) merge_up<HSZ, W * 64>(p, pl, pc, &merge_flag);
+        if (!whole) merge_up<HSZ, W * 64, NCMAX>(p, pl, pc, &merge_flag);
         t = pc.tile_end;
         if (t < t_end) __syncthreads();  // the reduction buffers are read before the next piece's stages reuse them
     }
 }
 
-template <int HSZ>
-size_t decode_tiles_lds_bytes(int G) {
-    using C = DecodeCfg<HSZ>;
+template <int HSZ, int NCB>
+size_t decode_tiles_lds_bytes(int NC) {
+    using C = DecodeCfg<HSZ, NCB>;
     const size_t stage = (size_t)C::W * C::STAGE * sizeof(uint16_t);
-    const size_t reduce = (size_t)(2 * C::W * 16 + C::W * G * (HSZ + 4)) * sizeof(float);
+    const size_t reduce = (size_t)(2 * C::W * C::NCMAX + C::W * NC * (HSZ + 4)) * sizeof(float);
     return stage > reduce ? stage : reduce;
 }
 
-size_t tiles_lds_bytes(int Hsz, int G) {
-    switch (Hsz) {
-        case 64: return decode_tiles_lds_bytes<64>(G);
-        case 128: return decode_tiles_lds_bytes<128>(G);
-        default: return decode_tiles_lds_bytes<256>(G);
+// Column blocks of 16 for NC query columns: 1, 2 or 4.
+inline int column_blocks(int NC) { return NC <= 16 ? 1 : (NC <= 32 ? 2 : 4); }
+
+// With timing events the launch goes through hipExtLaunchKernelGGL, which binds
+// the events to the kernel's own start and end timestamps (no separate marker
+// packets around it).
+template <int HSZ, bool FP8, bool PAGED, int NCB>
+hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+    using C = DecodeCfg<HSZ, NCB>;
+    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB>(p.NC);
+    static std::atomic<int> lds_set[kMaxLdsDevices];
+    hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED, NCB>), lds_set, lds);
+    if (e != hipSuccess) return e;
+    if (ev_begin || ev_end)
+        hipExtLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8, PAGED, NCB>), dim3(p.plan.P), dim3(C::W * 64),
+                              (uint32_t)lds, stream, ev_begin, ev_end, 0u, p);
+    else
+        hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8, PAGED, NCB>), dim3(p.plan.P), dim3(C::W * 64), lds, stream,
+                           p);
+    return hipGetLastError();
+}
+
+template <int HSZ, int NCB>
+hipError_t launch_tiles_n(const DecodeParams &p, bool fp8, hipStream_t stream, hipEvent_t ev_begin,
+                          hipEvent_t ev_end) {
+    const bool paged = p.block_table != nullptr;
+    if (fp8)
+        return paged ? launch_tiles_t<HSZ, true, true, NCB>(p, stream, ev_begin, ev_end)
+                     : launch_tiles_t<HSZ, true, false, NCB>(p, stream, ev_begin, ev_end);
+    return paged ? launch_tiles_t<HSZ, false, true, NCB>(p, stream, ev_begin, ev_end)
+                 : launch_tiles_t<HSZ, false, false, NCB>(p, stream, ev_begin, ev_end);
+}
+
+template <int HSZ>
+hipError_t launch_tiles_h(const DecodeParams &p, bool fp8, hipStream_t stream, hipEvent_t ev_begin,
+                          hipEvent_t ev_end) {
+    switch (column_blocks(p.NC)) {
+        case 1: return launch_tiles_n<HSZ, 1>(p, fp8, stream, ev_begin, ev_end);
+        case 2: return launch_tiles_n<HSZ, 2>(p, fp8, stream, ev_begin, ev_end);
+        default:
+            if constexpr (HSZ * 64 <= kMaxColumnElems) return launch_tiles_n<HSZ, 4>(p, fp8, stream, ev_begin, ev_end);
+            return hipErrorInvalidValue;
     }
 }
 
+template <int HSZ>
+hipError_t launch_merge_wide_h(const WideMergeParams &mp, hipStream_t stream, hipEvent_t ev_end) {
+    if (ev_end)
+        hipExtLaunchKernelGGL(merge_wide_kernel<HSZ>, dim3(mp.NC * HSZ / 16, mp.count), dim3(256), 0u, stream,
+                              nullptr, ev_end, 0u, mp);
+    else
+        hipLaunchKernelGGL(merge_wide_kernel<HSZ>, dim3(mp.NC * HSZ / 16, mp.count), dim3(256), 0, stream, mp);
+    return hipGetLastError();
+}
+
+template <int HSZ, int NCB>
+int occupancy_t(int NC) {
+    using C = DecodeCfg<HSZ, NCB>;
+    int blocks = 0;
+    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB>(NC);
+    const void *fn = reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false, false, NCB>);
+    if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false, false, NCB>, C::W * 64,
+                                                     lds) != hipSuccess)
+        return 1;
+    return blocks > 0 ? blocks : 1;
+}
+
+template <int HSZ>
+int occupancy_h(int NC) {
+    switch (column_blocks(NC)) {
+        case 1: return occupancy_t<HSZ, 1>(NC);
+        case 2: return occupancy_t<HSZ, 2>(NC);
+        default:
+            if constexpr (HSZ * 64 <= kMaxColumnElems) return occupancy_t<HSZ, 4>(NC);
+            return 1;
+    }
+}
+
+template <int HSZ>
+int tile_keys_h(int NC) {
+    switch (column_blocks(NC)) {
+        case 1: return DecodeCfg<HSZ, 1>::W * DecodeCfg<HSZ, 1>::KPB;
+        case 2: return DecodeCfg<HSZ, 2>::W * DecodeCfg<HSZ, 2>::KPB;
+        default: return DecodeCfg<HSZ, 4>::W * DecodeCfg<HSZ, 4>::KPB;
+    }
+}
+
+}  // namespace
+
 // Raises a kernel's dynamic-LDS limit (default 64 KiB; gfx950 has 160 KiB per
 // CU) to the largest size any call asks for, once per device and size, so
-// that launches captured into a graph make no attribute calls.
+// that launches captured into a graph make no attribute calls.  `done` holds
+// one entry per device (kMaxLdsDevices); the attribute call may run twice when
+// two threads race on a new size, which is harmless.
 hipError_t ensure_lds_limit(const void *fn, std::atomic<int> *done, size_t lds) {
     if (lds <= 65536) return hipSuccess;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::atomic<int> &d = done[dev < kMaxDevices ? dev : kMaxDevices - 1];
-    if (d.load(std::memory_order_acquire) >= (int)lds && dev < kMaxDevices) return hipSuccess;
+    std::atomic<int> &d = done[dev < kMaxLdsDevices ? dev : kMaxLdsDevices - 1];
+    if (d.load(std::memory_order_acquire) >= (int)lds && dev < kMaxLdsDevices) return hipSuccess;
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int cur = d.load(std::memory_order_relaxed);
@@ -793,67 +963,29 @@ hipError_t ensure_lds_limit(const void *fn, std::atomic<int> *done, size_t lds) 
     return hipSuccess;
 }
 
-template <int HSZ, bool FP8, bool PAGED>
-hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream) {
-    const size_t lds = decode_tiles_lds_bytes<HSZ>(p.NC);
-    static std::atomic<int> lds_set[kMaxDevices];
-    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED>), lds_set, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_tiles_kernel<HSZ, FP8, PAGED>), dim3(p.plan.P), dim3(DecodeCfg<HSZ>::W * 64), lds,
-                       stream, p);
-    return hipGetLastError();
-}
-
-template <int HSZ>
-hipError_t launch_tiles_h(const DecodeParams &p, bool fp8, hipStream_t stream) {
-    const bool paged = p.block_table != nullptr;
-    if (fp8) return paged ? launch_tiles_t<HSZ, true, true>(p, stream) : launch_tiles_t<HSZ, true, false>(p, stream);
-    return paged ? launch_tiles_t<HSZ, false, true>(p, stream) : launch_tiles_t<HSZ, false, false>(p, stream);
-}
-
-template <int HSZ>
-hipError_t launch_merge_wide_h(const WideMergeParams &mp, hipStream_t stream) {
-    hipLaunchKernelGGL(merge_wide_kernel<HSZ>, dim3(mp.NC * HSZ / 16, mp.count), dim3(256), 0, stream, mp);
-    return hipGetLastError();
-}
-
-template <int HSZ>
-int occupancy_t(int G) {
-    int blocks = 0;
-    const size_t lds = decode_tiles_lds_bytes<HSZ>(G);
-    if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false, false>, DecodeCfg<HSZ>::W * 64,
-                                                     decode_tiles_lds_bytes<HSZ>(G)) != hipSuccess)
-        return 1;
-    return blocks > 0 ? blocks : 1;
-}
-
-}  // namespace
-
-int decode_tile_keys(int Hsz) {
+int decode_tile_keys(int Hsz, int NC) {
     switch (Hsz) {
-        case 64: return DecodeCfg<64>::W * kKeysPerBlock;
-        case 128: return DecodeCfg<128>::W * kKeysPerBlock;
-        default: return DecodeCfg<256>::W * kKeysPerBlock;
+        case 64: return tile_keys_h<64>(NC);
+        case 128: return tile_keys_h<128>(NC);
+        default: return tile_keys_h<256>(NC);
     }
 }
 
-hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream) {
+hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream, hipEvent_t ev_begin,
+                               hipEvent_t ev_end) {
     switch (Hsz) {
-        case 64: return launch_tiles_h<64>(p, fp8, stream);
-        case 128: return launch_tiles_h<128>(p, fp8, stream);
-        case 256: return launch_tiles_h<256>(p, fp8, stream);
+        case 64: return launch_tiles_h<64>(p, fp8, stream, ev_begin, ev_end);
+        case 128: return launch_tiles_h<128>(p, fp8, stream, ev_begin, ev_end);
+        case 256: return launch_tiles_h<256>(p, fp8, stream, ev_begin, ev_end);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream) {
+hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream, hipEvent_t ev_end) {
     switch (Hsz) {
-        case 64: return launch_merge_wide_h<64>(mp, stream);
-        case 128: return launch_merge_wide_h<128>(mp, stream);
-        case 256: return launch_merge_wide_h<256>(mp, stream);
+        case 64: return launch_merge_wide_h<64>(mp, stream, ev_end);
+        case 128: return launch_merge_wide_h<128>(mp, stream, ev_end);
+        case 256: return launch_merge_wide_h<256>(mp, stream, ev_end);
         default: return hipErrorInvalidValue;
     }
 }
@@ -921,11 +1053,11 @@ hipError_t launch_merge_shards(const float *outs, const float *lses, int S, int6
     return hipGetLastError();
 }
 
-int decode_tiles_occupancy(int Hsz, int G) {
+int decode_tiles_occupancy(int Hsz, int NC) {
     switch (Hsz) {
-        case 64: return occupancy_t<64>(G);
-        case 128: return occupancy_t<128>(G);
-        default: return occupancy_t<256>(G);
+        case 64: return occupancy_h<64>(NC);
+        case 128: return occupancy_h<128>(NC);
+        default: return occupancy_h<256>(NC);
     }
 }
 

@@ -325,13 +325,9 @@ hipError_t launch_prefill_h(const uint16_t *q, const uint16_t *k, const uint16_t
     const int64_t nblocks = (int64_t)nqb * B * Hq;
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = (size_t)2 * PfDims<HSZ>::STAGE * sizeof(uint16_t);
-    static bool attr_set = false;  // above the default dynamic-LDS limit (gfx950 has 160 KiB per CU)
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_causal_kernel<HSZ>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<int> lds_set[kMaxLdsDevices];  // per device: above the 64 KiB default
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(prefill_causal_kernel<HSZ>), lds_set, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_causal_kernel<HSZ>, dim3((unsigned)nblocks), dim3(PfDims<HSZ>::NT), lds, stream, q, k, v, out, B,
                        ISL, Hq, KH, scale_log2, nqb);
     return hipGetLastError();

@@ -2,18 +2,25 @@
 """Benchmark of the GQA decode/prefill library on one MI355X.
 
 A step is one ``attn_decode_ex`` call (host plan + one decode kernel, whose last CTA per
-split head merges the partial states) on the Llama-3-8B-shaped decode workload: B=16,
-Hq=32, KH=8 (G=4), Hsz=128, every request at 8192 cached tokens, bf16 K/V ~ N(0,1), fp32
-output (``--workload`` picks another decode workload for the headline).  ``value`` is
-the achieved HBM bandwidth in algorithmic bytes (every cached K and V byte, the query
-and the output, each counted once) per second of step time over back-to-back steps,
-with the inputs already resident in HBM.  The K/V caches are rotated over enough
-copies that each step reads bytes the 256 MiB last-level cache does not hold from the
-previous step.
+split head merges the partial states, + the merge kernel of heads split over more than
+16 CTAs when there is one) on the ragged continuous-batch decode workload, the largest
+single-GPU configuration: B=32, Hq=32, KH=8 (G=4), Hsz=128, per-request context lengths
+drawn log-uniform in [512, 65536] (seed 0: 501,182 cached tokens, 2.05 GB of K+V), bf16
+K/V ~ N(0,1), fp32 output (``--workload`` picks another decode workload for the
+headline).  ``value`` is the achieved HBM bandwidth in algorithmic bytes (every cached K
+and V byte, the query and the output, each counted once) per second of step time:
+HIP events around K back-to-back steps, with the inputs already resident in HBM.  The K/V
+caches are rotated over enough copies that each step reads bytes the 256 MiB last-level
+cache does not hold from the previous step.
 
-The same run also times: the decode kernel alone (HIP events recorded on the launch
-stream around each launch -> the ``roofline`` object), the other decode workloads
-(long-context MQA with x1 and x8 scores, the ragged batch, FP8 and paged caches,
+``roofline`` takes the same bytes over the decode kernels' own time: a second pass of K
+steps with timing events bound to the start of the tile kernel and the end of the step's
+last decode kernel (hipExtLaunchKernel, so no marker packets enter the stream), averaged
+over the launches.  ``rooflines`` holds the same object for every decode workload (HBM)
+and for causal prefill (MFMA).
+
+The same run also times the other decode workloads
+(Llama-3-8B-shaped, long-context MQA with x1 and x8 scores, FP8 and paged caches,
 multi-token decode), stream-K against the fixed split, device against host lengths, the
 ragged (G, Hsz) sweep at fixed total KV bytes, causal prefill (MFMA TFLOP/s) at head
 dimensions 128, 64 and 256, one KV-sequence shard and the shard merge, a copy and a read
@@ -97,7 +104,8 @@ def log(msg: str) -> None:
 def bench_decode(shape, steps: int, warmup: int, hev: HipEvents, rotate: bool = True, schedule: int = 0,
                  fp8: bool = False, block_size: int = 0, device_seqlens: bool = False, lse: bool = False):
     """Times `steps` decode steps back to back (value), then the same number again with HIP
-    events recorded on the launch stream around every decode-kernel launch (roofline).
+    timing events bound to each step's decode kernels (roofline: first kernel's start to the
+    last kernel's end).
     With device_seqlens the lengths sit in a device tensor and the plan is built on the device."""
     import torch
 
@@ -393,8 +401,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--headline-only", action="store_true", help="time only the headline decode workload")
-    ap.add_argument("--workload", default="llama3_8b",
-                    help="decode workload of the headline line (llama3_8b, long_mqa, long_mqa_x8, ragged, tiny)")
+    ap.add_argument("--workload", default="ragged",
+                    help="decode workload of the headline line (ragged, llama3_8b, long_mqa, long_mqa_x8, tiny)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -427,7 +435,7 @@ def main():
     prefill = None
     prefill_dims = []
     if not args.headline_only:
-        for name in [n for n in ["llama3_8b", "long_mqa", "long_mqa_x8", "ragged"] if n != head.name]:
+        for name in [n for n in ["ragged", "llama3_8b", "long_mqa", "long_mqa_x8"] if n != head.name]:
             log(f"decode {name} ...")
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
@@ -517,7 +525,27 @@ def main():
         cpu = cpu_baseline(head)
         log(f"  {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
 
-    traffic = committed_traffic(f"decode_{head.name}", r["bytes_per_step"])
+    def roofline_hbm(res):
+        name = res["workload"]
+        return {"workload": name, "bound": "hbm", "achieved": round(res["kernel_GBps"], 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(res["kernel_GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": committed_traffic(f"decode_{name}", res["bytes_per_step"]),
+                "kernel": f"decode_tiles_kernel<{res['Hsz']}>",
+                "timing": "events bound to the tile kernel's start and the step's last decode kernel's end "
+                          "(the wide-head merge kernel is inside when the step launches one)",
+                "kernel_us": round(res["kernel_us"], 2), "us_per_step": round(res["us_per_step"], 2),
+                "bytes_per_launch": res["bytes_per_step"]}
+
+    rooflines = [roofline_hbm(x) for x in [r] + [o for o in others if "_paged" not in o["workload"]]]
+    for pf in [prefill] + prefill_dims:
+        if pf:
+            rooflines.append({"workload": pf["workload"], "bound": "mfma", "achieved": round(pf["TFLOPs"], 1),
+                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pf["mfma_frac_of_bf16_peak"], 4),
+                              "traffic": None, "kernel": f"prefill_causal_kernel<{pf['Hsz']}>",
+                              "kernel_us": round(pf["us_per_step"], 2),
+                              "timing": "HIP events around back-to-back launches (one kernel per step)",
+                              "flops_per_launch": pf["flops_per_step"]})
+    head_roof = roofline_hbm(r)
     line = {
         "metric": "decode attn achieved HBM GB/s (% peak) + us/step; prefill MFMA TFLOP/s",
         "value": round(r["GBps"], 1),
@@ -536,10 +564,9 @@ def main():
                    "sum_kvsl": int(sum(head.seqlens)), "out_dtype": "fp32", "parallelism": "single_gpu"},
         "frac_of_peak_hbm": round(r["frac_of_peak"], 4),
         "us_per_step": round(r["us_per_step"], 2),
-        "roofline": {"bound": "hbm", "achieved": round(r["kernel_GBps"], 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(r["kernel_GBps"] / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": f"decode_tiles_kernel<{head.Hsz}>",
-                     "kernel_us": round(r["kernel_us"], 2)},
+        "roofline": {k: head_roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                               "kernel_us", "bytes_per_launch")},
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "other_decode_workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in o.items()}
                                    for o in others],

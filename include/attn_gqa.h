@@ -50,7 +50,8 @@ enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
     ATTN_ERR_SHAPE = -2,       /* inconsistent sizes (B <= 0, Hq % KH != 0, L_b < 0 or > stride, ...) */
-    ATTN_ERR_UNSUPPORTED = -3, /* valid but not implemented (Hsz not in {64,128,256}, G > 16, B > 256, ...) */
+    ATTN_ERR_UNSUPPORTED = -3, /* valid but not implemented (Hsz not in {64,128,256}, too many query columns,
+                                  B > 256, ...) */
     ATTN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = -5,   /* caller workspace too small */
     ATTN_ERR_HIP = -6          /* a HIP runtime call failed; see attn_last_error() */
@@ -58,8 +59,13 @@ enum attn_status {
 
 /* Largest batch the decode planner accepts (its plan travels in kernel arguments). */
 #define ATTN_MAX_BATCH 256
-/* Largest group size G = Hq / KH the decode kernel holds in one workgroup. */
-#define ATTN_MAX_GROUP 16
+/* Query columns one decode workgroup holds: the G = Hq / KH query heads of a kv
+ * head times q_len drafted tokens.  G * q_len <= ATTN_MAX_COLUMNS, and
+ * G * q_len * Hsz <= ATTN_MAX_COLUMN_ELEMS (64 columns at Hsz 64 or 128, 32 at
+ * Hsz 256): every column's output accumulator stays in registers while K and V
+ * stream past, so one pass over the cache serves all of them. */
+#define ATTN_MAX_COLUMNS 64
+#define ATTN_MAX_COLUMN_ELEMS 8192
 /* Largest number of persistent decode workgroups (num_ctas). */
 #define ATTN_MAX_CTAS 4096
 /* Bytes at the start of a decode workspace that hold the merge counters
@@ -158,9 +164,13 @@ typedef struct attn_decode_args {
                                  k times (k = floor(B*KH / slots), at most 4) when the
                                  (request, kv head) segments outnumber the slots at
                                  least twice.  Must be 0 for the fixed split. */
-    hipEvent_t ev_tiles_begin;/* optional: recorded on `stream` right before the decode kernel */
-    hipEvent_t ev_tiles_end;  /* optional: recorded right after the decode kernel (before the
-                                 merge kernel of heads split over more than 16 workgroups) */
+    hipEvent_t ev_tiles_begin;/* optional timing event, bound to the start of the decode tile
+                                 kernel (launched through hipExtLaunchKernel, so no marker
+                                 packet is added to the stream) */
+    hipEvent_t ev_tiles_end;  /* optional timing event, bound to the end of the call's last decode
+                                 kernel: the merge kernel of heads split over more than 16
+                                 workgroups when one runs, the tile kernel otherwise.  With
+                                 device seqlens the plan kernel in front is not included. */
     int schedule;             /* ATTN_SCHEDULE_*; 0 = AUTO */
     int num_splits;           /* fixed split: chunks per (request, kv head); 0 = fill the GPU once.
                                  With more than one split, B*KH*num_splits <= ATTN_MAX_CTAS. */
@@ -181,7 +191,8 @@ typedef struct attn_decode_args {
      * the target model checks gamma drafted tokens at once).  With q_len = gamma > 1, q
      * and out are [B][Hq][gamma][Hsz], the cache already holds the drafted tokens as
      * the last gamma of each context, and query t attends keys 0 .. L_b - gamma + t.
-     * Needs G * gamma <= ATTN_MAX_GROUP and L_b = 0 or L_b >= gamma. */
+     * Needs G * gamma within the column limits (ATTN_MAX_COLUMNS, ATTN_MAX_COLUMN_ELEMS)
+     * and L_b = 0 or L_b >= gamma. */
     int q_len;                /* 0 or 1 = one query token per request */
     /* Device seqlens.  Nonzero: `seqlens` is a DEVICE int32 [B] that the call never
      * reads on the host.  A one-workgroup kernel builds the LeanTile plan on the
@@ -206,11 +217,17 @@ int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
 
 /*
  * Bytes of workspace attn_decode_ex needs for these sizes when it runs with
- * `num_ctas` workgroups (0 = the library's default for the current device;
- * that query initialises the HIP runtime): ATTN_DECODE_COUNTER_BYTES of merge
- * counters, ATTN_DECODE_PLAN_BYTES for a plan built on the device, then 2
- * partial slots per workgroup of (G*Hsz + 2G) floats rounded up to 16 bytes.
- * Returns 0 for unsupported sizes.
+ * `num_ctas` workgroups: ATTN_DECODE_COUNTER_BYTES of merge counters,
+ * ATTN_DECODE_PLAN_BYTES for a plan built on the device, then 2 partial slots
+ * per workgroup of (G*Hsz + 2G) floats rounded up to 16 bytes.
+ *   num_ctas > 0   exactly that many workgroups: a stream-K call with that
+ *                  num_ctas, or a fixed split with num_ctas = B*KH*num_splits.
+ *   num_ctas = 0   enough for every call that leaves the count to the library on
+ *                  the current device (this query initialises the HIP runtime):
+ *                  the larger of the stream-K default and the fixed split's
+ *                  default, so any schedule (AUTO included) with num_ctas = 0 and
+ *                  num_splits = 0 fits.
+ * Returns 0 for unsupported sizes (and when the device query fails).
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas);
 
@@ -244,8 +261,11 @@ int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows,
  *                                 causal mask), scale 1/sqrt(Hsz), fp32
  *                                 accumulation, rounded to bf16 once at the end
  * QK^T runs on bf16 MFMA; the PV product runs on fp16 MFMA with V converted
- * bf16 -> fp16 (exact for |v| < 65504; larger |v| is outside the contract) and
- * the softmax weights rounded to fp16.
+ * bf16 -> fp16 and
+ * the softmax weights rounded to fp16.  The conversion of V is exact for bf16 values
+ * in fp16's normal range (2^-14 <= |v| < 65504) and for zero; smaller nonzero |v| lose
+ * mantissa bits (an absolute error below 2^-24 per element); |v| >= 65504 is outside
+ * the contract.
  * Source: co-design page, sections "프리필과 디코드의 차이" and "FlashAttention과
  * GEMM 모양" (prefill is the large, compute-bound matmul form of the same
  * fused kernel).  Hsz must be 64, 128 or 256 (ATTN_ERR_UNSUPPORTED otherwise).

@@ -68,7 +68,8 @@ def call_decode(q=FAKE, k=FAKE, v=FAKE, sl=(4, 4), B=2, Hq=8, KH=2, Hsz=128, out
     (dict(KH=0), A.ATTN_ERR_SHAPE),
     (dict(Hsz=96), A.ATTN_ERR_UNSUPPORTED),
     (dict(Hsz=512), A.ATTN_ERR_UNSUPPORTED),
-    (dict(Hq=64, KH=2), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=256, KH=2), A.ATTN_ERR_UNSUPPORTED),              # G = 128 > 64 query columns
+    (dict(Hq=128, KH=2, Hsz=256), A.ATTN_ERR_UNSUPPORTED),     # 64 columns x 256 > 8192
     (dict(B=257, sl=(1,) * 257), A.ATTN_ERR_UNSUPPORTED),
     (dict(q=FAKE + 2), A.ATTN_ERR_ALIGN),
     (dict(out=FAKE + 4), A.ATTN_ERR_ALIGN),
@@ -99,8 +100,9 @@ def ex_args(**kw):
     (dict(scale=float("inf")), A.ATTN_ERR_SHAPE),
     (dict(scale=float("nan")), A.ATTN_ERR_SHAPE),
     (dict(workspace=FAKE + 4, workspace_bytes=1 << 20), A.ATTN_ERR_ALIGN),
-    (dict(workspace=FAKE, workspace_bytes=16, num_ctas=4), A.ATTN_ERR_WORKSPACE),
-    (dict(workspace=FAKE, workspace_bytes=32768, num_ctas=4), A.ATTN_ERR_WORKSPACE),  # counters only
+    # 2 x 2 segments of 16 LeanTiles over 6 CTAs: heads are split, so slots are needed
+    (dict(seqlens=(4096, 4096), workspace=FAKE, workspace_bytes=16, num_ctas=6), A.ATTN_ERR_WORKSPACE),
+    (dict(seqlens=(4096, 4096), workspace=FAKE, workspace_bytes=32768, num_ctas=6), A.ATTN_ERR_WORKSPACE),
     (dict(num_ctas=4097), A.ATTN_ERR_UNSUPPORTED),
     (dict(schedule=3), A.ATTN_ERR_SHAPE),
     (dict(schedule=-1), A.ATTN_ERR_SHAPE),
@@ -120,7 +122,8 @@ def ex_args(**kw):
     (dict(block_size=16), A.ATTN_ERR_SHAPE),                      # block geometry without a table
     (dict(q_len=-1), A.ATTN_ERR_SHAPE),
     (dict(out_lse=FAKE + 2), A.ATTN_ERR_ALIGN),
-    (dict(q_len=5), A.ATTN_ERR_UNSUPPORTED),                      # G * q_len = 20 > 16 query columns
+    (dict(q_len=17), A.ATTN_ERR_UNSUPPORTED),                     # G * q_len = 68 > 64 query columns
+    (dict(Hsz=256, q_len=9), A.ATTN_ERR_UNSUPPORTED),             # 36 columns x 256 > 8192
     (dict(Hq=2, KH=2, q_len=5), A.ATTN_ERR_SHAPE),                 # 4 cached keys < 5 query tokens
     (dict(seqlens=(4, 70), block_table=FAKE, block_size=16, max_blocks_per_seq=4, num_blocks=8),
      A.ATTN_ERR_SHAPE),                                           # 70 keys > 4 blocks x 16
@@ -192,7 +195,10 @@ def test_workspace_bytes_formula():
     assert A.attn_decode_workspace_bytes(1, 8, 1, 64, A.ATTN_MAX_CTAS + 1) == 0
     # multi-token: slots hold G * q_len states
     assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 4, 100) == C + 2 * 100 * ((16 * 128 + 32 + 3) & ~3) * 4
-    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 5, 100) == 0  # 20 columns
+    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 5, 100) == C + 2 * 100 * ((20 * 128 + 40 + 3) & ~3) * 4
+    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 128, 17, 100) == 0  # 68 columns
+    assert A.attn_decode_multi_workspace_bytes(16, 32, 8, 256, 9, 100) == 0   # 36 columns x 256
+    assert A.attn_decode_workspace_bytes(1, 64, 1, 128, 10) == C + 2 * 10 * ((64 * 128 + 128 + 3) & ~3) * 4
 
 
 def test_python_binding_validates_cache_capacity():
@@ -201,3 +207,43 @@ def test_python_binding_validates_cache_capacity():
     with pytest.raises(TypeError):
         A.attn_decode(torch.zeros(1, 8, 128, dtype=torch.bfloat16), torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16),
                       torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16), [4])
+
+
+def _no_gpu() -> bool:
+    import torch
+    return torch.cuda.device_count() == 0  # counts devices without initialising one
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a host without a GPU: there every HIP runtime call fails")
+def test_hip_failure_after_validation_is_reported():
+    # Valid arguments pass validation; the first HIP runtime call after it (the device query for
+    # the default workgroup count) fails on a host without a GPU, and the failure comes back as
+    # ATTN_ERR_HIP with the call and the HIP error text, not as a crash or a silent success.
+    lib = A.lib()
+    assert call_decode() == A.ATTN_ERR_HIP
+    msg = lib.attn_last_error().decode()
+    assert "hipGetDevice" in msg and "(" in msg, msg
+    # an explicit stream-K count needs no device query; the failure then comes from the launch path
+    a, _sl = ex_args(num_ctas=1, schedule=A.ATTN_SCHEDULE_STREAM_K)
+    assert lib.attn_decode_ex(ctypes.byref(a), None) == A.ATTN_ERR_HIP
+    assert lib.attn_last_error().decode() != ""
+    cus, lds = ctypes.c_int(), ctypes.c_int()
+    assert lib.attn_device_info(ctypes.byref(cus), ctypes.byref(lds)) == A.ATTN_ERR_HIP
+    # the size query reports failure as 0 bytes
+    assert A.attn_decode_workspace_bytes(2, 8, 2, 128, 0) == 0
+
+
+def test_workspace_check_uses_the_clamped_cta_count():
+    # 2 requests x 2 kv heads x 1 tile = 4 tiles: an explicit num_ctas of 64 is clamped to 4,
+    # no head is split, so no workspace is needed and a tiny caller workspace is accepted by
+    # validation (on a GPU-less host the call then fails at its first HIP call, not with
+    # ATTN_ERR_WORKSPACE)
+    a, _sl = ex_args(num_ctas=64, schedule=A.ATTN_SCHEDULE_STREAM_K, workspace=FAKE, workspace_bytes=16)
+    st = A.lib().attn_decode_ex(ctypes.byref(a), None) if _no_gpu() else None
+    if st is not None:
+        assert st == A.ATTN_ERR_HIP
+    # 2 requests of 4096 keys over 64 CTAs at T=256: heads are split, the workspace is checked
+    # against the final count before any HIP call
+    a, _sl = ex_args(seqlens=(4096, 4096), num_ctas=64, tile_keys=256, schedule=A.ATTN_SCHEDULE_STREAM_K,
+                     workspace=FAKE, workspace_bytes=32768 + 8192)
+    assert A.lib().attn_decode_ex(ctypes.byref(a), None) == A.ATTN_ERR_WORKSPACE
