@@ -8,9 +8,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
-#include <vector>
 #include <string>
 #include <utility>
 
@@ -50,24 +50,28 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;      // library-owned partial-state buffers
-std::map<std::pair<int, int>, int> g_default_ctas;          // (device, Hsz*1000+NC) -> resident CTAs
+// Resident decode workgroups per (device, head dimension, query columns), 0 until
+// first queried.  A fixed table, so a decode call allocates no host memory.
+constexpr int kResidentDevices = 64;
+std::atomic<int> g_resident[kResidentDevices][3][attn::kMaxColumns + 1];
 
-int device_default_ctas(int Hsz, int G, int *out) {
+int device_default_ctas(int Hsz, int NC, int *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_pair(dev, Hsz * 1000 + G);
-    auto it = g_default_ctas.find(key);
-    if (it != g_default_ctas.end()) {
-        *out = it->second;
+    if (dev < 0 || dev >= kResidentDevices) return fail(ATTN_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kResidentDevices);
+    std::atomic<int> &slot = g_resident[dev][Hsz == 64 ? 0 : (Hsz == 128 ? 1 : 2)][NC];
+    int r = slot.load(std::memory_order_acquire);
+    if (r > 0) {
+        *out = r;
         return ATTN_OK;
     }
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(MultiprocessorCount)");
-    const int occ = attn::decode_tiles_occupancy(Hsz, G);
-    *out = g_default_ctas[key] = cus * occ;
+    r = cus * attn::decode_tiles_occupancy(Hsz, NC);
+    slot.store(r, std::memory_order_release);  // concurrent first queries store the same value
+    *out = r;
     return ATTN_OK;
 }
 
@@ -377,9 +381,10 @@ int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource s
         schedule = ATTN_SCHEDULE_STREAM_K;
         if (!dev_sl && a->num_ctas == 0 && p.plan.N > 0) {
             if ((st = query_resident()) != ATTN_OK) return st;
-            std::vector<int64_t> heap((size_t)resident);
-            const int64_t even = (p.plan.N + resident - 1) / resident;
-            if (plan_whole_segments_makespan(p.plan, resident, heap.data()) <= even)
+            int64_t heap[attn::kMaxCtas];  // the selector's min-heap, one entry per resident slot
+            const int R = resident < attn::kMaxCtas ? resident : attn::kMaxCtas;
+            const int64_t even = (p.plan.N + R - 1) / R;
+            if (plan_whole_segments_makespan(p.plan, R, heap) <= even)
                 schedule = ATTN_SCHEDULE_FIXED_SPLIT;
         }
     }

@@ -628,19 +628,6 @@ __device__ __forceinline__ int piece_blocks(const LeanPiece &pc) {
     return (pc.key_end - pc.key_begin + KPB - 1) / KPB;
 }
 
-// The waves of a CTA take the blocks of a piece in any order (the softmax merge
-// is order-free), so each CTA starts its walk at its own rotation of the piece:
-// block i of the walk is block (i + rot) mod nblk.  CTA ranges of equal-length
-// contexts sit at power-of-two strides, and without the rotation every CTA
-// would read the same offset of its range, hence the same HBM channels, at the
-// same moment.
-__device__ __forceinline__ int piece_rotation(int c, int nblk) { return (int)(((unsigned)c * 13u) % (unsigned)nblk); }
-
-__device__ __forceinline__ int rotated_block(int i, int rot, int nblk) {
-    const int j = i + rot;
-    return j < nblk ? j : j - nblk;
-}
-
 template <int HSZ, bool FP8, bool PAGED, int NCB>
 __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_kernel(const DecodeParams p) {
     using C = DecodeCfg<HSZ, NCB>;
@@ -697,11 +684,9 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
     LeanPiece pc0 = {};
     if (t < t_end) {
         pc0 = uniform_piece(plan_piece_at(pl, t, t_end));
-        const int nblk0 = piece_blocks<KPB>(pc0);
-        if (wave < nblk0)
+        if (wave < piece_blocks<KPB>(pc0))
             load_block<HSZ, FP8, PAGED, KPB>(st, piece_rows<HSZ, FP8, PAGED>(p, pl, pc0.b, pc0.kh),
-                                             pc0.key_begin + rotated_block(wave, piece_rotation(c, nblk0), nblk0) * KPB,
-                                             pc0.key_end - 1, lane);
+                                             pc0.key_begin + wave * KPB, pc0.key_end - 1, lane);
     }
 
     // Requests with an empty context own no tiles: their output rows are zero.
@@ -754,9 +739,7 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
         // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
         int blk = wave;
-        const int rot = piece_rotation(c, nblk);
-        if (!first_piece && blk < nblk)
-            load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + rotated_block(blk, rot, nblk) * KPB, klast, lane);
+        if (!first_piece && blk < nblk) load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + blk * KPB, klast, lane);
         first_piece = false;
         while (blk < nblk) {
             store_block<HSZ, FP8, KPB>(st, stage, lane);
@@ -765,11 +748,10 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
             int nxt = 0;
             if (lane == 0) nxt = atomicAdd(&blk_next, 1);
             nxt = __builtin_amdgcn_readfirstlane(nxt);
-            if (nxt < nblk)
-                load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + rotated_block(nxt, rot, nblk) * KPB, klast, lane);
+            if (nxt < nblk) load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + nxt * KPB, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ, NCB>(stage, qop, pc.key_begin + rotated_block(blk, rot, nblk) * KPB, kmax, col, grp,
-                                    p.scale_log2, m_run, l_run, oacc);
+            process_block<HSZ, NCB>(stage, qop, pc.key_begin + blk * KPB, kmax, col, grp, p.scale_log2, m_run, l_run,
+                                    oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             blk = nxt;
