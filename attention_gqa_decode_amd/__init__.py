@@ -26,6 +26,7 @@ ATTN_MAX_COLUMN_ELEMS = 8192
 ATTN_MAX_CTAS = 4096
 ATTN_DECODE_COUNTER_BYTES = 32768
 ATTN_DECODE_PLAN_BYTES = 8192
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 ATTN_SCHEDULE_AUTO = 0
 ATTN_SCHEDULE_STREAM_K = 1
 ATTN_SCHEDULE_FIXED_SPLIT = 2
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.restype = _I
     L.attn_decode_ex.argtypes = [ctypes.POINTER(attn_decode_args), _P]
     L.attn_decode_ex.restype = _I
+    L.attn_decode_noalloc.argtypes = [ctypes.POINTER(attn_decode_args), _P]
+    L.attn_decode_noalloc.restype = _I
     L.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.attn_decode_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -277,6 +280,26 @@ def attn_decode_ex(q, k_cache, v_cache, seqlens, out=None, *, scale=0.0, tile_ke
     a.ev_tiles_end = ev_tiles_end
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
     return _keep[1]
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, out, *, scale=0.0, tile_keys=0, num_ctas=0,
+                        schedule=ATTN_SCHEDULE_AUTO, num_splits=0, k_scale=0.0, v_scale=0.0, out_lse=None,
+                        stream=None):
+    """``attn_decode_noalloc``: ``attn_decode_ex`` with the library's fixed device scratch as
+    its workspace (no device allocation in the call).  ``out`` must be given: this call
+    allocates nothing, torch tensors included.  ``q`` is [B][Hq][Hsz], or
+    [B][Hq][q_len][Hsz] for multi-token decode."""
+    if out is None:
+        raise ValueError("attn_decode_noalloc needs a preallocated out tensor")
+    multi = q.dim() == 4
+    a, keep = _decode_args(q, k_cache, v_cache, seqlens, out, q_len=q.shape[2] if multi else 1, multi=multi,
+                           paged=False, block_table=None, scale=scale, tile_keys=tile_keys, num_ctas=num_ctas,
+                           schedule=schedule, num_splits=num_splits, k_scale=k_scale, v_scale=v_scale,
+                           out_lse=out_lse, workspace=None)
+    if multi:
+        a.q_len = q.shape[2]
+    _check(lib().attn_decode_noalloc(ctypes.byref(a), _stream_handle(stream)))
+    return keep[1]
 
 
 def attn_merge_shards(outs, lses, out=None, lse_out=None, stream=None):

@@ -248,7 +248,36 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int KH, int Hsz, int num_ctas)
 namespace {
 
 // Where the partial-state workspace of a decode call comes from.
-enum class WorkspaceSource { Caller, Library };
+enum class WorkspaceSource { Caller, Library, Scratch };
+
+// The workspace of attn_decode_noalloc: a device array of fixed size in the
+// library's code object, so that entry point never allocates.  Each device the
+// library runs on holds its own copy until the process ends.  `scratch` is the
+// host-side stand-in of the array; the device address of a device's copy comes
+// from hipGetSymbolAddress (scratch_pointer) and is the only address used.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+static_assert(ATTN_NOALLOC_SCRATCH_BYTES == kScratchBytes, "scratch size mismatch");
+
+constexpr int kScratchDevices = 64;
+void *g_scratch_ptr[kScratchDevices];  // per device, set once under g_mu
+
+// The current device's copy of `scratch`, resolved once per device.
+int scratch_pointer(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices) return fail(ATTN_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
 
 int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource src) {
     if (!a) return fail(ATTN_ERR_NULL, "args is NULL");
@@ -423,12 +452,24 @@ int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource s
     const size_t need = split ? attn::decode_workspace_bytes(P, p.NC, a->Hsz) : 0;
     if (split && src == WorkspaceSource::Caller && a->workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace_bytes=%zu < %zu needed for %d workgroups", a->workspace_bytes, need, P);
+    if (split && src == WorkspaceSource::Scratch && need > kScratchBytes)
+        return fail(ATTN_ERR_WORKSPACE, "this call needs %zu bytes of partial-state workspace; attn_decode_noalloc "
+                    "holds at most %zu (ATTN_NOALLOC_SCRATCH_BYTES)", need, kScratchBytes);
 
     // ---- HIP calls from here on ----
     if (split) {
         char *w = nullptr;
         if (src == WorkspaceSource::Caller) {
             w = static_cast<char *>(a->workspace);
+        } else if (src == WorkspaceSource::Scratch) {
+            void *sp = nullptr;
+            if ((st = scratch_pointer(&sp)) != ATTN_OK) return st;
+            w = static_cast<char *>(sp);
+            // The array keeps the last call's contents: clear the arrival counters
+            // this call uses (a fill kernel rather than a memset, so a captured
+            // graph replays it correctly).
+            const hipError_t ez = attn::launch_zero_fill(w, (size_t)2 * P * sizeof(int), stream);
+            if (ez != hipSuccess) return fail_hip(ez, "scratch counter fill");
         } else {
             void *lw = nullptr;
             if ((st = library_workspace(stream, need, &lw)) != ATTN_OK) return st;
@@ -488,6 +529,14 @@ int attn_decode_ex(const attn_decode_args *a, hipStream_t stream) {
     g_last_error.clear();
     if (a && a->workspace) return decode_impl(a, stream, WorkspaceSource::Caller);
     return decode_impl(a, stream, WorkspaceSource::Library);
+}
+
+int attn_decode_noalloc(const attn_decode_args *a, hipStream_t stream) {
+    g_last_error.clear();
+    if (a && (a->workspace || a->workspace_bytes))
+        return fail(ATTN_ERR_SHAPE, "attn_decode_noalloc uses the library's fixed scratch: workspace must be NULL and "
+                    "workspace_bytes 0");
+    return decode_impl(a, stream, WorkspaceSource::Scratch);
 }
 
 int attn_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out, float *lse_out,

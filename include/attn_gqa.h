@@ -216,6 +216,28 @@ typedef struct attn_decode_args {
 int attn_decode_ex(const attn_decode_args *args, hipStream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ *   args   as for attn_decode_ex, except that workspace must be NULL and
+ *          workspace_bytes 0 (ATTN_ERR_SHAPE otherwise): the partial states,
+ *          merge counters and device-built plan live in a fixed device array of
+ *          ATTN_NOALLOC_SCRATCH_BYTES inside the library, one copy per device,
+ *          held from the library's load until the process ends.
+ *   stream as for attn_decode_ex; the same kernels run, plus one small kernel
+ *          that clears the counters the call uses.
+ * Returns ATTN_ERR_WORKSPACE, before anything is enqueued, when the call needs
+ * more partial-state memory than the array holds (attn_decode_multi_workspace_bytes
+ * gives the need); calls that split no head need none.  All calls on one device
+ * share its array: calls that may overlap on one device (different streams, or
+ * several host threads on one stream) race and give wrong results; calls
+ * ordered on one stream do not.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_noalloc(const attn_decode_args *args, hipStream_t stream);
+
+/*
  * Bytes of workspace attn_decode_ex needs for these sizes when it runs with
  * `num_ctas` workgroups: ATTN_DECODE_COUNTER_BYTES of merge counters,
  * ATTN_DECODE_PLAN_BYTES for a plan built on the device, then 2 partial slots
