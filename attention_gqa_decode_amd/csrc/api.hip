@@ -366,7 +366,9 @@ int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource s
         st = build_plan(a->seqlens, a->B, a->KH, T, stride, &p.plan);
         if (st != ATTN_OK) return st;
     }
-    p.plan_dev = nullptr;
+    p.seqlens_dev = nullptr;
+    p.wide_count = nullptr;
+    p.wide_list = nullptr;
     p.q = static_cast<const uint16_t *>(a->q);
     p.k = static_cast<const uint16_t *>(a->k_cache);
     p.v = static_cast<const uint16_t *>(a->v_cache);
@@ -478,21 +480,19 @@ int decode_impl(const attn_decode_args *a, hipStream_t stream, WorkspaceSource s
         p.counters = reinterpret_cast<int *>(w);
         p.ws = reinterpret_cast<float *>(w + attn::kCounterBytes + attn::kPlanAreaBytes);
         if (dev_sl) {
+            // every CTA builds the plan from the device lengths; CTA 0 lists the wide
+            // heads in the plan area for the merge kernel
             char *area = w + attn::kCounterBytes;
-            p.plan_dev = reinterpret_cast<const LeanPlan *>(area);
-            wide.count_dev = reinterpret_cast<const int *>(area + attn::kWideCountOffset);
-            wide.head_dev = reinterpret_cast<const attn::WideHead *>(area + attn::kWideListOffset);
+            p.seqlens_dev = a->seqlens;
+            p.wide_count = reinterpret_cast<int *>(area + attn::kWideCountOffset);
+            p.wide_list = reinterpret_cast<attn::WideHead *>(area + attn::kWideListOffset);
+            wide.count_dev = p.wide_count;
+            wide.head_dev = p.wide_list;
         }
     }
 
     hipError_t e;
     if (dev_sl) {
-        const attn::PlanBase base = {a->B, a->KH, T, p.plan.mode, p.plan.splits, P};
-        char *area = reinterpret_cast<char *>(const_cast<LeanPlan *>(p.plan_dev));
-        e = attn::launch_plan_device(a->seqlens, base, stride, reinterpret_cast<LeanPlan *>(area),
-                                     reinterpret_cast<int *>(area + attn::kWideCountOffset),
-                                     reinterpret_cast<attn::WideHead *>(area + attn::kWideListOffset), stream);
-        if (e != hipSuccess) return fail_hip(e, "device plan kernel launch");
         // the most heads that can be split over more than kMergeFanIn CTAs
         const int64_t segs = (int64_t)a->B * a->KH;
         int64_t most = p.plan.mode == kPlanFixedSplit ? (p.plan.splits > attn::kMergeFanIn ? segs : 0)

@@ -47,7 +47,12 @@ struct DecodeParams {
     int max_blocks_per_seq;
     int log2_block_size;
     int num_blocks;
-    const LeanPlan *plan_dev;  // non-NULL: the plan was built on the device (seqlens in device memory)
+    // Device seqlens (non-NULL): every CTA builds the plan from these lengths, and
+    // `plan` carries only B, KH, T, mode, splits and the launched P; CTA 0 lists
+    // the heads split over more than kMergeFanIn CTAs in wide_list / *wide_count.
+    const int32_t *seqlens_dev;
+    int *wide_count;
+    struct WideHead *wide_list;
     LeanPlan plan;
 };
 
@@ -84,8 +89,8 @@ struct WideMergeParams {
 
 // Workspace layout: int counters[2 * kMaxCtas] (a fixed-size region, so its
 // place never depends on P), then a plan area that a call with device seqlens
-// fills on the device (the LeanPlan, then the wide-head count and list), then
-// float slots[2P][slot_floats].
+// uses for the wide-head count and list (written by the decode kernel's CTA 0
+// for the merge kernel), then float slots[2P][slot_floats].
 constexpr size_t kCounterBytes = (size_t)2 * kMaxCtas * sizeof(int);
 constexpr size_t kPlanAreaBytes = 8192;
 constexpr size_t kWideCountOffset = 4096;  // within the plan area
@@ -107,14 +112,6 @@ hipError_t ensure_lds_limit(const void *fn, std::atomic<int> *done, size_t lds);
 hipError_t launch_decode_tiles(const DecodeParams &p, int Hsz, bool fp8, hipStream_t stream,
                                hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t stream, hipEvent_t ev_end = nullptr);
-// Builds the LeanPlan of `base` (B, KH, T, mode, splits, P) for the device
-// seqlens on the device, clamping each L_b into [0, stride], and lists the wide
-// heads; one workgroup.
-struct PlanBase {
-    int B, KH, T, mode, splits, P;  // P: launched CTAs (stream-K) or B*KH*splits (fixed split)
-};
-hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int64_t stride, LeanPlan *plan_out,
-                              int *wide_count, WideHead *wide, hipStream_t stream);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_merge_shards(const float *outs, const float *lses, int S, int64_t rows, int Hsz, float *out,
                                float *lse_out, hipStream_t stream);

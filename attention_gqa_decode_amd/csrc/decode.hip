@@ -91,7 +91,7 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
 //    room for more).
 //  * W waves per workgroup: 8 (two per SIMD, 256 registers each) where the
 //    wave fits, else 4 (one per SIMD, up to 512 registers with the AGPRs).
-template <int HSZ, int NCB>
+template <int HSZ, int NCB, bool FP8>
 struct DecodeCfg {
     static constexpr int KPB = HSZ == 256 || HSZ * NCB >= 512 ? 16 : 32;
     static constexpr int KB = KPB / 16;                  // 16-key MFMA row blocks per wave block
@@ -211,15 +211,15 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterp
 // (col, grp) its keys after kmax[cb] (the piece's end, or the causal limit of
 // the lane's drafted token) are masked.  Each K and V operand read from LDS
 // serves all NCB column blocks.
-template <int HSZ, int NCB>
+template <int HSZ, int NCB, int KPB>
 __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[NCB][HSZ / 32],
                                               int key0, const int (&kmax)[NCB], int col, int grp,
                                               float scale_log2, float (&m_run)[NCB], float (&l_run)[NCB],
                                               f32x4 (&oacc)[NCB][HSZ / 16]) {
-    using C = DecodeCfg<HSZ, NCB>;
+    using C = DecodeCfg<HSZ, NCB, false>;  // the stage layout does not depend on the cache type
     constexpr int NS = C::NS;
     constexpr int ND = C::ND;
-    constexpr int KB = C::KB;
+    constexpr int KB = KPB / 16;
     const float NEG_INF = -__builtin_inff();
     const uint16_t *krow = stage + col * C::RS + 8 * grp;  // key col of 16-key row block 0
     // BMM1: S^T[key][c] for keys key0 + 16kb + 4grp + i in lane (c = 16cb + col, grp)
@@ -274,7 +274,7 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
     // transposing reads.  Lane (i, grp) gets V[4 grp + j][16 db + i] (and, with
     // 32-key blocks, V[16 + 4 grp + j][16 db + i]), j = 0..3: the key order of
     // this lane's S^T accumulator, so P needs no shuffle.
-    const uint16_t *vstage = stage + C::KPB * C::RS;
+    const uint16_t *vstage = stage + KPB * C::RS;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
         const i16x4 a = v_cols(vstage, C::RS, 4 * grp, 16 * db, col);
@@ -514,69 +514,90 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const WideMergeParams m
     }
 }
 
-// The LeanPlan of a call whose seqlens live in device memory, built on the
-// device so that the call needs no host read of them (and can be captured in a
-// graph): L_b clamped into [0, stride], the tile prefix (one scan over the
-// batch), N, P = min(launched CTAs, N) for stream-K, and the heads split over
-// more than kMergeFanIn CTAs for merge_wide_kernel.  The same numbering as the
-// host planner (plan.h), so the tile kernel cannot tell the two apart.
-static_assert(ATTN_MAX_BATCH == 256, "plan_device_kernel maps one thread to each request slot");
-__global__ __launch_bounds__(256) void plan_device_kernel(const int32_t *seqlens, const PlanBase base, int64_t stride,
-                                                          LeanPlan *plan_out, int *wide_count, WideHead *wide) {
-    __shared__ LeanPlan lp;
-    __shared__ int64_t part[256];
-    __shared__ int nwide;
+// The LeanPlan of a call whose seqlens live in device memory, built by every
+// CTA of the decode kernel into its own LDS (so the call needs no host read of
+// the lengths, no extra kernel, and can be captured in a graph): L_b clamped
+// into [0, stride], the tile prefix (one scan over the batch, in wave 0 with
+// lane shuffles), N, and P = min(launched CTAs, N) for stream-K.  The same
+// numbering as the host planner (plan.h), so the rest of the kernel cannot tell
+// the two apart.  `base` carries B, KH, T, the mode, the splits and the
+// launched P.  The caller's barrier publishes `lp`.
+static_assert(ATTN_MAX_BATCH == 256, "the device plan scans 256 request slots");
+template <int NT>
+__device__ void build_plan_lds(const int32_t *seqlens, const LeanPlan &base, int64_t stride, LeanPlan &lp) {
+    static_assert(NT >= 64, "one wave builds the plan");
     const int tid = threadIdx.x;
-    const int B = base.B, KH = base.KH;
-    int64_t tiles = 0;
-    int L = 0;
-    if (tid < B) {
-        L = seqlens[tid];
-        L = L < 0 ? 0 : (L > stride ? (int)stride : L);
-        tiles = (int64_t)KH * ((L + (int64_t)base.T - 1) / base.T);
+    if (tid < 64) {
+        // wave 0: lane i takes requests 4i .. 4i+3, then one inclusive scan over the lanes
+        const int B = base.B, KH = base.KH;
+        int64_t tiles[4], own = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * tid + j;
+            int L = 0;
+            if (b < B) {
+                L = seqlens[b];
+                L = L < 0 ? 0 : (L > stride ? (int)stride : L);
+            }
+            lp.seqlen[b] = L;
+            tiles[j] = (int64_t)KH * ((L + (int64_t)base.T - 1) / base.T);
+            own += tiles[j];
+        }
+        int64_t incl = own;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t v = __shfl_up(incl, off);
+            if (tid >= off) incl += v;
+        }
+        const int64_t N = __shfl(incl, 63);
+        int64_t pre = incl - own;  // tiles before request 4i
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * tid + j;
+            lp.tile_prefix[b] = (int32_t)(b < B ? pre : N);
+            pre += tiles[j];
+        }
+        if (tid == 0) {
+            lp.tile_prefix[256] = (int32_t)N;
+            lp.B = B;
+            lp.KH = KH;
+            lp.T = base.T;
+            lp.N = N;
+            lp.mode = base.mode;
+            lp.splits = base.splits;
+            lp.P = base.mode == kPlanStreamK ? (int)(N < base.P ? (N > 0 ? N : 1) : base.P) : base.P;
+        }
     }
-    lp.seqlen[tid] = L;
-    part[tid] = tiles;
+}
+
+// The heads of a device-built plan split over more than kMergeFanIn CTAs, for
+// merge_wide_kernel (which runs after the decode kernel): written by CTA 0
+// once its own pieces are done.  All NT threads call it; *count gets the total.
+template <int NT>
+__device__ void write_wide_list(const LeanPlan &lp, int *nwide, int *count, WideHead *wide) {
+    const int tid = threadIdx.x;
+    if (tid == 0) *nwide = 0;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the tiles per request
-        const int64_t v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    const int64_t N = part[255];
-    lp.tile_prefix[tid] = (int32_t)(tid < B ? part[tid] - tiles : N);
-    if (tid == 0) {
-        lp.tile_prefix[256] = (int32_t)N;
-        lp.B = B;
-        lp.KH = KH;
-        lp.T = base.T;
-        lp.N = N;
-        lp.mode = base.mode;
-        lp.splits = base.splits;
-        lp.P = base.mode == kPlanStreamK ? (int)(N < base.P ? (N > 0 ? N : 1) : base.P) : base.P;
-        nwide = 0;
-    }
-    __syncthreads();
-    for (int s = tid; s < B * KH; s += 256) {
-        const int b = s / KH, kh = s - b * KH;
+    // A stream-K CTA owns at least floor(N/P) tiles, so a segment spread over more
+    // than kMergeFanIn CTAs has more than (kMergeFanIn - 1) floor(N/P) tiles:
+    // shorter ones are skipped without locating their CTAs.
+    const int64_t min_wide = lp.mode == kPlanStreamK ? (int64_t)(kMergeFanIn - 1) * (lp.N / lp.P) : 0;
+    for (int s = tid; s < lp.B * lp.KH; s += NT) {
+        const int b = s / lp.KH, kh = s - b * lp.KH;
         const int nb = plan_tiles_per_segment(lp, b);
-        if (nb == 0) continue;
+        if (nb == 0 || nb <= min_wide) continue;
         const int64_t s0 = lp.tile_prefix[b] + (int64_t)kh * nb;
         const SegmentCtas sc = plan_segment_ctas(lp, s0, s0 + nb);
         if (sc.n > kMergeFanIn) {
-            const int i = atomicAdd(&nwide, 1);  // at most kMaxWideHeads (see WideMergeParams)
+            const int i = atomicAdd(nwide, 1);  // at most kMaxWideHeads (see WideMergeParams)
             if (i < kMaxWideHeads) {
                 wide[i].bkh = b | kh << 8;
                 wide[i].cta = sc.c_lo | (sc.n - 1) << 12 | (plan_slot(lp, sc.c_lo, s0) & 1) << 24;
             }
         }
     }
-    const int *src = reinterpret_cast<const int *>(&lp);
-    int *dst = reinterpret_cast<int *>(plan_out);
-    for (int i = tid; i < (int)(sizeof(LeanPlan) / sizeof(int)); i += 256) dst[i] = src[i];
     __syncthreads();
-    if (tid == 0) *wide_count = nwide < kMaxWideHeads ? nwide : kMaxWideHeads;
+    if (tid == 0) *count = *nwide < kMaxWideHeads ? *nwide : kMaxWideHeads;
 }
 
 // K/V rows of the context of request b under kv head kh.
@@ -629,8 +650,8 @@ __device__ __forceinline__ int piece_blocks(const LeanPiece &pc) {
 }
 
 template <int HSZ, bool FP8, bool PAGED, int NCB>
-__global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_kernel(const DecodeParams p) {
-    using C = DecodeCfg<HSZ, NCB>;
+__global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_tiles_kernel(const DecodeParams p) {
+    using C = DecodeCfg<HSZ, NCB, FP8>;
     constexpr int NS = C::NS;
     constexpr int ND = C::ND;
     constexpr int W = C::W;
@@ -659,19 +680,17 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
     // costs a single round of vector loads instead of chains of dependent
     // scalar loads from the argument segment.
     __shared__ LeanPlan plan_lds;
-    {
+    if (p.seqlens_dev) {  // device seqlens: the plan is built here (the stages serve as scan scratch)
+        build_plan_lds<W * 64>(p.seqlens_dev, p.plan, p.kv_stride, plan_lds);
+        if (threadIdx.x == 0) blk_next = W;
+    } else {
         constexpr int WORDS = (int)(sizeof(LeanPlan) / sizeof(int));
         int *dst = reinterpret_cast<int *>(&plan_lds);
-        if (p.plan_dev) {  // built on the device from device seqlens
-            const int *src = reinterpret_cast<const int *>(p.plan_dev);
-            for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
-        } else {
-            const int *src = reinterpret_cast<const int *>(&p.plan);
-            for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
-        }
+        const int *src = reinterpret_cast<const int *>(&p.plan);
+        for (int i = threadIdx.x; i < WORDS; i += W * 64) dst[i] = src[i];
         if (threadIdx.x == 0) blk_next = W;
-        __syncthreads();
     }
+    __syncthreads();
     const LeanPlan &pl = plan_lds;
     // a plan built on the device uses min(P, N) of the launched CTAs
     if (c >= __builtin_amdgcn_readfirstlane(pl.P)) return;
@@ -750,8 +769,8 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < nblk) load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + nxt * KPB, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ, NCB>(stage, qop, pc.key_begin + blk * KPB, kmax, col, grp, p.scale_log2, m_run, l_run,
-                                    oacc);
+            process_block<HSZ, NCB, KPB>(stage, qop, pc.key_begin + blk * KPB, kmax, col, grp, p.scale_log2, m_run,
+                                         l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             blk = nxt;
@@ -824,11 +843,15 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB>::W * 64)) void decode_tiles_ke
         t = pc.tile_end;
         if (t < t_end) __syncthreads();  // the reduction buffers are read before the next piece's stages reuse them
     }
+    if (p.seqlens_dev && c == 0) {
+        __syncthreads();  // the last piece's merge has read merge_flag
+        write_wide_list<W * 64>(pl, &merge_flag, p.wide_count, p.wide_list);
+    }
 }
 
-template <int HSZ, int NCB>
+template <int HSZ, int NCB, bool FP8>
 size_t decode_tiles_lds_bytes(int NC) {
-    using C = DecodeCfg<HSZ, NCB>;
+    using C = DecodeCfg<HSZ, NCB, FP8>;
     const size_t stage = (size_t)C::W * C::STAGE * sizeof(uint16_t);
     const size_t reduce = (size_t)(2 * C::W * C::NCMAX + C::W * NC * (HSZ + 4)) * sizeof(float);
     return stage > reduce ? stage : reduce;
@@ -842,8 +865,8 @@ inline int column_blocks(int NC) { return NC <= 16 ? 1 : (NC <= 32 ? 2 : 4); }
 // packets around it).
 template <int HSZ, bool FP8, bool PAGED, int NCB>
 hipError_t launch_tiles_t(const DecodeParams &p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-    using C = DecodeCfg<HSZ, NCB>;
-    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB>(p.NC);
+    using C = DecodeCfg<HSZ, NCB, FP8>;
+    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB, FP8>(p.NC);
     static std::atomic<int> lds_set[kMaxLdsDevices];
     hipError_t e =
         ensure_lds_limit(reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, FP8, PAGED, NCB>), lds_set, lds);
@@ -892,9 +915,9 @@ hipError_t launch_merge_wide_h(const WideMergeParams &mp, hipStream_t stream, hi
 
 template <int HSZ, int NCB>
 int occupancy_t(int NC) {
-    using C = DecodeCfg<HSZ, NCB>;
+    using C = DecodeCfg<HSZ, NCB, false>;
     int blocks = 0;
-    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB>(NC);
+    const size_t lds = decode_tiles_lds_bytes<HSZ, NCB, false>(NC);
     const void *fn = reinterpret_cast<const void *>(decode_tiles_kernel<HSZ, false, false, NCB>);
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_tiles_kernel<HSZ, false, false, NCB>, C::W * 64,
@@ -914,12 +937,16 @@ int occupancy_h(int NC) {
     }
 }
 
+// Default LeanTile: every wave's first round of blocks.
+template <class C>
+constexpr int tile_keys_of() { return C::W * C::KPB; }
+
 template <int HSZ>
 int tile_keys_h(int NC) {
     switch (column_blocks(NC)) {
-        case 1: return DecodeCfg<HSZ, 1>::W * DecodeCfg<HSZ, 1>::KPB;
-        case 2: return DecodeCfg<HSZ, 2>::W * DecodeCfg<HSZ, 2>::KPB;
-        default: return DecodeCfg<HSZ, 4>::W * DecodeCfg<HSZ, 4>::KPB;
+        case 1: return tile_keys_of<DecodeCfg<HSZ, 1, false>>();
+        case 2: return tile_keys_of<DecodeCfg<HSZ, 2, false>>();
+        default: return tile_keys_of<DecodeCfg<HSZ, 4, false>>();
     }
 }
 
@@ -970,13 +997,6 @@ hipError_t launch_merge_wide(const WideMergeParams &mp, int Hsz, hipStream_t str
         case 256: return launch_merge_wide_h<256>(mp, stream, ev_end);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_plan_device(const int32_t *seqlens, const PlanBase &base, int64_t stride, LeanPlan *plan_out,
-                              int *wide_count, WideHead *wide, hipStream_t stream) {
-    hipLaunchKernelGGL(plan_device_kernel, dim3(1), dim3(256), 0, stream, seqlens, base, stride, plan_out, wide_count,
-                       wide);
-    return hipGetLastError();
 }
 
 // Merge of S decode outputs over disjoint key ranges of the same rows (KV
