@@ -48,9 +48,12 @@
 #include <hip/hip_ext.h>
 
 #include <atomic>
+#include <type_traits>
 
 namespace attn {
 namespace {
+
+constexpr float kLazyMax = 8.f;  // lazy running-max threshold in log2 units (weights <= 256)
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -103,22 +106,27 @@ struct DecodeCfg {
     static constexpr int STAGE = 2 * KPB * RS;           // bf16 per wave: K rows then V rows
 };
 
-// One wave's next block in registers: fully coalesced 16-byte loads (lane l of
-// load j reads chunk (64j + l) of the block, row-major over keys), marked
+// One wave's next block in registers: fully coalesced loads (lane l of load j
+// reads chunk (64j + l) of the block, row-major over keys), marked
 // non-temporal because every byte is used exactly once.  Rows past klast are
-// clamped re-reads of row klast (their scores are masked later).  An element
-// is 2 bytes (bf16) or 1 byte (FP8 E4M3): a 16-byte chunk holds 8 or 16 of them.
+// clamped re-reads of row klast (their scores are masked later).  A chunk is 8
+// elements: 16 bytes of bf16, or 8 bytes of FP8 E4M3 codes, which widen to the
+// same 16 bytes of bf16, so every lane parks one contiguous 16-byte run per
+// chunk and the LDS stores of a wave cover whole rows without bank conflicts.
 template <int HSZ, bool FP8, int KPB>
 struct KvCfg {
-    static constexpr int EPC = FP8 ? 16 : 8;                          // elements per 16-byte chunk
+    static constexpr int EPC = 8;                                     // elements per chunk
     static constexpr int CPR = HSZ / EPC;                             // chunks per row
     static constexpr int LOADS = 2 * KPB * CPR / 64;                  // chunks per lane per block (K + V)
     static_assert(KPB * CPR % 64 == 0, "a block's chunks split evenly over the lanes");
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int HSZ, bool FP8, int KPB>
 struct Staged {
-    u32x4 r[KvCfg<HSZ, FP8, KPB>::LOADS];
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type chunk_t;
+    chunk_t r[KvCfg<HSZ, FP8, KPB>::LOADS];
 };
 
 // Where the rows of one (request, kv head) context live.  Contiguous: row j of
@@ -154,26 +162,22 @@ __device__ __forceinline__ void load_block(Staged<HSZ, FP8, KPB> &st, const KvRo
         int key = key0 + c / K::CPR;
         key = key < klast ? key : klast;
         const int64_t off = kv.row_offset(key, HSZ * EB) + K::EPC * (c % K::CPR) * EB;
-        st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kv.kbase + off));
-        st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kv.vbase + off));
+        using chunk_t = typename Staged<HSZ, FP8, KPB>::chunk_t;
+        st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const chunk_t *>(kv.kbase + off));
+        st.r[HALF + j] = __builtin_nontemporal_load(reinterpret_cast<const chunk_t *>(kv.vbase + off));
     }
 }
 
-// 16 E4M3 codes -> 16 bf16 (two 16-byte halves), exactly: every E4M3 value is a
-// bf16 value, and the conversion runs with scale 1.
-__device__ __forceinline__ void fp8x16_to_bf16(const u32x4 &w, u32x4 &lo, u32x4 &hi) {
+// 8 E4M3 codes -> 8 bf16 (16 bytes), exactly: every E4M3 value is a bf16
+// value, and the conversion runs with scale 1.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2 &w) {
+    u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-        if (i < 2) {
-            lo[2 * i] = a;
-            lo[2 * i + 1] = b;
-        } else {
-            hi[2 * i - 4] = a;
-            hi[2 * i - 3] = b;
-        }
+    for (int i = 0; i < 2; ++i) {
+        r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+        r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
     }
+    return r;
 }
 
 // Registers -> this wave's LDS stage as bf16, rows padded by 16 bytes
@@ -190,13 +194,8 @@ __device__ __forceinline__ void store_block(const Staged<HSZ, FP8, KPB> &st, uin
         uint16_t *kd = stage + row * RS + col;
         uint16_t *vd = stage + (KPB + row) * RS + col;
         if constexpr (FP8) {
-            u32x4 a, b;
-            fp8x16_to_bf16(st.r[j], a, b);
-            *reinterpret_cast<u32x4 *>(kd) = a;
-            *reinterpret_cast<u32x4 *>(kd + 8) = b;
-            fp8x16_to_bf16(st.r[HALF + j], a, b);
-            *reinterpret_cast<u32x4 *>(vd) = a;
-            *reinterpret_cast<u32x4 *>(vd + 8) = b;
+            *reinterpret_cast<u32x4 *>(kd) = fp8x8_to_bf16(st.r[j]);
+            *reinterpret_cast<u32x4 *>(vd) = fp8x8_to_bf16(st.r[HALF + j]);
         } else {
             *reinterpret_cast<u32x4 *>(kd) = st.r[j];
             *reinterpret_cast<u32x4 *>(vd) = st.r[HALF + j];
@@ -209,11 +208,16 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterp
 // BMM1 -> online softmax -> BMM2 for one staged block of KPB keys of one wave.
 // Column block cb holds MFMA columns 16 cb .. 16 cb + 15; in every lane
 // (col, grp) its keys after kmax[cb] (the piece's end, or the causal limit of
-// the lane's drafted token) are masked.  Each K and V operand read from LDS
+// the lane's drafted token) are masked when `mask` is set (uniform: the block
+// reaches past some column's limit).  Each K and V operand read from LDS
 // serves all NCB column blocks.
+// The running max is a lazily moved reference: it moves only when a block's
+// max exceeds it by more than kLazyMax (log2 units), so the weights stay at
+// most 2^kLazyMax and O and l are rescaled only on the rare blocks that move
+// it.  Any reference gives the same softmax, so this is exact up to rounding.
 template <int HSZ, int NCB, int KPB>
 __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x8 (&qop)[NCB][HSZ / 32],
-                                              int key0, const int (&kmax)[NCB], int col, int grp,
+                                              int key0, const int (&kmax)[NCB], bool mask, int col, int grp,
                                               float scale_log2, float (&m_run)[NCB], float (&l_run)[NCB],
                                               f32x4 (&oacc)[NCB][HSZ / 16]) {
     using C = DecodeCfg<HSZ, NCB, false>;  // the stage layout does not depend on the cache type
@@ -246,16 +250,22 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = key0 + 16 * kb + 4 * grp + i;
-                const float xv = key <= kmax[cb] ? sc[cb][kb][i] * scale_log2 : NEG_INF;
+                float xv = sc[cb][kb][i] * scale_log2;
+                if (mask) xv = key0 + 16 * kb + 4 * grp + i <= kmax[cb] ? xv : NEG_INF;
                 x[4 * kb + i] = xv;
                 mx = fmaxf(mx, xv);
             }
         mx = wave_max_over_groups(mx);
-        const float m_new = fmaxf(m_run[cb], mx);
+        const bool move = mx > m_run[cb] + kLazyMax;  // always true on a column's first key
+        const float m_new = move ? mx : m_run[cb];
         // -inf only while a drafted token's column has seen no key yet (its limit lies before this block)
         const float m_use = m_new == NEG_INF ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
+        if (__builtin_amdgcn_ballot_w64(move)) {  // alpha is 1 on the columns that did not move
+            const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
+            l_run[cb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) oacc[cb][db] *= alpha;
+        }
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4 * KB; ++i) {
@@ -265,10 +275,8 @@ __device__ __forceinline__ void process_block(const uint16_t *stage, const bf16x
             phi[cb][i] = hi;
             plo[cb][i] = (__bf16)(pv - (float)hi);
         }
-        l_run[cb] = l_run[cb] * alpha + ps;
+        l_run[cb] += ps;
         m_run[cb] = m_new;
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[cb][db] *= alpha;
     }
     // BMM2: the V^T operand comes straight out of the row-major V stage through
     // transposing reads.  Lane (i, grp) gets V[4 grp + j][16 db + i] (and, with
@@ -751,6 +759,9 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_til
             const int climit = pl.seqlen[pc.b] - p.qlen + ccol / G;
             kmax[cb] = klast < climit ? klast : climit;
         }
+        // blocks ending at or before kmin (every column's limit) need no mask
+        const int climit0 = pl.seqlen[pc.b] - p.qlen;  // the limit of drafted token 0
+        const int kmin = klast < climit0 ? klast : climit0;
         // Block w starts on wave w; every wave claims its next block from an
         // LDS counter when it starts computing one, so waves whose loads come
         // back sooner take more blocks and all waves of the CTA finish within
@@ -769,7 +780,8 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_til
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < nblk) load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + nxt * KPB, klast, lane);
             __builtin_amdgcn_sched_barrier(0);
-            process_block<HSZ, NCB, KPB>(stage, qop, pc.key_begin + blk * KPB, kmax, col, grp, p.scale_log2, m_run,
+            const int key0 = pc.key_begin + blk * KPB;
+            process_block<HSZ, NCB, KPB>(stage, qop, key0, kmax, key0 + KPB - 1 > kmin, col, grp, p.scale_log2, m_run,
                                          l_run, oacc);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
