@@ -726,31 +726,43 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_til
             for (int e = threadIdx.x; e < p.Hq * p.qlen; e += W * 64) p.lse[(int64_t)b * p.Hq * p.qlen + e] = -__builtin_inff();
     }
 
+    // Column c = 16 cb + col holds query token c / G of head kh G + c % G of the
+    // piece (q is [B][Hq][qlen][Hsz]); columns past NC are zero.
+    bf16x8 qop[NCB][NS];
+    auto load_q = [&](const LeanPiece &pq) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int cc = 16 * cb + col;
+            const int ccol = cc < NC ? cc : 0;
+            const uint16_t *qrow = p.q + (((int64_t)pq.b * p.Hq + pq.kh * G + ccol % G) * p.qlen + ccol / G) * HSZ;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 z = {};
+                qop[cb][s] = cc < NC ? load_row8(qrow + 32 * s + 8 * grp) : z;
+            }
+        }
+    };
+    // At HSZ = 256 with 8 waves the next piece's queries would not fit beside the
+    // epilogue's registers: there they are loaded when the piece starts.
+    constexpr bool kPrefetchQ = !(HSZ == 256 && W == 8);
     bool first_piece = true;
+    LeanPiece pc_next = pc0;
     while (t < t_end) {
-        const LeanPiece pc = first_piece ? pc0 : uniform_piece(plan_piece_at(pl, t, t_end));
+        const LeanPiece pc = pc_next;
         const KvRows<PAGED> kv = piece_rows<HSZ, FP8, PAGED>(p, pl, pc.b, pc.kh);
         const int h0 = pc.kh * G;
 
-        // Column c = 16 cb + col holds query token c / G of head h0 + c % G (q is
-        // [B][Hq][qlen][Hsz]); columns past NC are zero.
-        bf16x8 qop[NCB][NS];
         float m_run[NCB];  // running max (log2 domain) of column c
         float l_run[NCB];  // this lane's share of the running sum
         f32x4 oacc[NCB][ND];  // O[c][16*db + 4*grp + i]
         int kmax[NCB];
         const int nblk = piece_blocks<KPB>(pc);
         const int klast = pc.key_end - 1;
+        if (first_piece || !kPrefetchQ) load_q(pc);  // else requested before the previous epilogue
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int cc = 16 * cb + col;
             const int ccol = cc < NC ? cc : 0;
-            const uint16_t *qrow = p.q + (((int64_t)pc.b * p.Hq + h0 + ccol % G) * p.qlen + ccol / G) * HSZ;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                bf16x8 z = {};
-                qop[cb][s] = cc < NC ? load_row8(qrow + 32 * s + 8 * grp) : z;
-            }
             m_run[cb] = NEG_INF;
             l_run[cb] = 0.f;
 #pragma unroll
@@ -769,7 +781,6 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_til
         // the current one is computed out of the wave's LDS stage; LDS traffic
         // of one wave executes in issue order, so no barrier is needed.
         int blk = wave;
-        if (!first_piece && blk < nblk) load_block<HSZ, FP8, PAGED, KPB>(st, kv, pc.key_begin + blk * KPB, klast, lane);
         first_piece = false;
         while (blk < nblk) {
             store_block<HSZ, FP8, KPB>(st, stage, lane);
@@ -786,6 +797,17 @@ __global__ __launch_bounds__((DecodeCfg<HSZ, NCB, FP8>::W * 64)) void decode_til
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             blk = nxt;
+        }
+
+        // The staging registers and the query operands are free now: the next
+        // piece's first block and queries are requested before this piece's
+        // epilogue, whose barriers and stores then hide their latency.
+        if (pc.tile_end < t_end) {
+            pc_next = uniform_piece(plan_piece_at(pl, pc.tile_end, t_end));
+            if (wave < piece_blocks<KPB>(pc_next))
+                load_block<HSZ, FP8, PAGED, KPB>(st, piece_rows<HSZ, FP8, PAGED>(p, pl, pc_next.b, pc_next.kh),
+                                                 pc_next.key_begin + wave * KPB, pc_next.key_end - 1, lane);
+            if constexpr (kPrefetchQ) load_q(pc_next);
         }
 
         // ---- merge the W wave states of this piece ----
