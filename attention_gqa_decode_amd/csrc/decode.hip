@@ -89,14 +89,17 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
 // Launch shape for head dimension HSZ and NCB blocks of 16 MFMA columns (the
 // query columns: G heads x q_len drafted tokens, up to 16 NCB of them).
 //  * KPB keys per wave block: 32, or 16 at HSZ = 256 (so one block is 16 KiB
-//    of bf16 K+V at every head dimension and its staging takes 64 registers
-//    per lane) and with 64 columns at HSZ = 128 (whose accumulators leave no
-//    room for more).
+//    of bf16 K+V there and its staging takes 64 registers per lane), with 64
+//    columns at HSZ = 128 (whose accumulators leave no room for more), and for
+//    bf16 at HSZ = 128 with up to 16 columns: there the 8 KiB blocks measured
+//    1-3% faster than 16 KiB ones (each wave's load-to-use chain is shorter and
+//    the LeanTile finer), while at HSZ = 64, with more columns and for FP8 the
+//    larger block was as fast or faster.
 //  * W waves per workgroup: 8 (two per SIMD, 256 registers each) where the
 //    wave fits, else 4 (one per SIMD, up to 512 registers with the AGPRs).
 template <int HSZ, int NCB, bool FP8>
 struct DecodeCfg {
-    static constexpr int KPB = HSZ == 256 || HSZ * NCB >= 512 ? 16 : 32;
+    static constexpr int KPB = HSZ == 256 || HSZ * NCB >= 512 || (HSZ == 128 && NCB == 1 && !FP8) ? 16 : 32;
     static constexpr int KB = KPB / 16;                  // 16-key MFMA row blocks per wave block
     static constexpr int W = NCB == 1 ? 8 : (NCB == 2 && HSZ == 64 ? 8 : 4);
     static constexpr int NCMAX = 16 * NCB;               // MFMA columns

@@ -122,7 +122,9 @@ def test_caller_workspace_matches_library_workspace():
     ws = torch.zeros(need // 4, dtype=torch.float32, device="cuda")
     a = gpu_decode(q, k, v, sl, num_ctas=64, workspace=ws)
     b = gpu_decode(q, k, v, sl, num_ctas=64)
-    np.testing.assert_array_equal(a, b)
+    # the same plan; waves claim blocks dynamically, so only the summation order may differ
+    assert np.abs(a - b).max() <= 1e-5
+    assert np.abs(a - oracle_decode(q, k, v, sl, 2, 1 / math.sqrt(128))).max() <= DECODE_TOL
     counters = ws[: A.ATTN_DECODE_COUNTER_BYTES // 4].view(torch.int32)
     assert int(counters.abs().sum()) == 0, "merge counters must be left at zero"
     with pytest.raises(A.AttnError) as e:
@@ -171,7 +173,7 @@ def test_simple_entry_matches_ex():
     a = A.attn_decode(q, k, v, sl)
     torch.cuda.synchronize()
     b = gpu_decode(q, k, v, sl)
-    np.testing.assert_array_equal(a.cpu().double().numpy(), b)
+    assert np.abs(a.cpu().double().numpy() - b).max() <= 1e-5  # same plan, dynamic block order
 
 
 def test_cache_capacity_larger_than_contexts():
