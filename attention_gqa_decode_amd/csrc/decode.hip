@@ -11,17 +11,21 @@
 //    over resident CTAs; partial (m, l, O) states merged by rescaling to the
 //    common max.  The work split itself lives in plan.h.
 //
-// gfx950 mapping.  A workgroup is 8 wave64s (4 at Hsz = 256).  Inside a piece
-// (one (b, kv head) context range) the waves take 32-key blocks round-robin
-// and never synchronise with each other until the piece ends.  Per block a wave
+// gfx950 mapping.  A workgroup is 8 wave64s, or 4 where the query columns'
+// accumulators need more than 256 registers per wave (DecodeCfg).  Inside a
+// piece (one (b, kv head) context range) each wave claims blocks of 16 or 32
+// keys from an LDS counter and never synchronises with the other waves until
+// the piece ends.  Per block a wave
 //   1. streams the K and V rows from HBM with fully coalesced, non-temporal
-//      16-byte loads (each load instruction covers whole 128-byte lines; a
+//      loads (16 bytes of bf16, or 8 bytes of FP8 codes that are widened to
+//      bf16 on the way; each load instruction covers whole 128-byte lines; a
 //      measured 6.7-7.1 TB/s pattern, against ~6.0 TB/s when each instruction
 //      takes 64 bytes of 16 rows) into registers, while the previous block is
 //      being computed, and parks them in its own LDS stage;
 //   2. BMM1 on v_mfma_f32_16x16x32_bf16 with A = K (16 keys x 32 d, read from
-//      the stage), B = Q^T (32 d x 16 heads, rows >= G are zero): S^T lands
-//      with the head index on lanes and four consecutive keys per lane;
+//      the stage), B = Q^T (32 d x 16 query columns: the G heads times the
+//      drafted tokens, in blocks of 16, columns past them zero): S^T lands
+//      with the column index on lanes and four consecutive keys per lane;
 //   3. online softmax in the log2 domain; the row max over the block needs two
 //      cross-lane steps (lanes 16 and 32 apart);
 //   4. V^T straight from the row-major V stage: transposing LDS reads

@@ -77,23 +77,63 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def kernel_sources_digest() -> str:
-    h = hashlib.sha256()
-    for f in ["decode.hip", "plan.h", "common.h"]:
-        with open(os.path.join(ROOT, "attention_gqa_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def _elf_sections(blob: bytes, base: int = 0) -> dict:
+    """Section name -> (file offset, size) of the 64-bit little-endian ELF at blob[base:]."""
+    import struct
+    shoff, = struct.unpack_from("<Q", blob, base + 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", blob, base + 0x3A)
+    hdr = lambda i: struct.unpack_from("<IIQQQQ", blob, base + shoff + i * shentsize)
+    stroff = hdr(shstrndx)[4]
+    out = {}
+    for i in range(shnum):
+        name, _, _, _, off, size = hdr(i)
+        end = blob.index(b"\0", base + stroff + name)
+        out[blob[base + stroff + name:end].decode()] = (base + off, size)
+    return out
+
+
+def kernel_code_digest():
+    """sha256 (16 hex digits) of the gfx950 machine code and kernel descriptors (the device
+    code object's .text and .rodata) in the built library, or None without one.  Counter
+    summaries carry it, so they stay valid across edits that leave the kernels unchanged
+    (comments) and lapse on any change to the code the GPU runs."""
+    import struct
+    lib = os.path.join(ROOT, "attention_gqa_decode_amd", "libattn_gqa.so")
+    if not os.path.exists(lib):
+        return None
+    blob = open(lib, "rb").read()
+    sec_off, sec_size = _elf_sections(blob)[".hip_fatbin"]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    h, found = hashlib.sha256(), 0
+    off = blob.find(magic, sec_off, sec_off + sec_size)  # one bundle per source file
+    while off >= 0:
+        n, = struct.unpack_from("<Q", blob, off + len(magic))
+        pos = off + len(magic) + 8
+        for _ in range(n):
+            e_off, _, t_len = struct.unpack_from("<QQQ", blob, pos)
+            triple = blob[pos + 24:pos + 24 + t_len].decode()
+            pos += 24 + t_len
+            if triple.endswith("gfx950"):
+                secs = _elf_sections(blob, off + e_off)
+                for s in (".text", ".rodata"):
+                    o, size = secs.get(s, (0, 0))
+                    h.update(blob[o:o + size])
+                found += 1
+        off = blob.find(magic, pos, sec_off + sec_size)
+    return h.hexdigest()[:16] if found else None
 
 
 def committed_traffic(name: str, launches_bytes: float):
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    """HBM bytes per launch from the committed counter summary, if it was taken on the kernels
+    the library holds now (same kernel_code_digest)."""
     path = os.path.join(ROOT, "profiles", f"{name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_hash = re.search(r"kernel_sources_digest:\s*([0-9a-f]+)", text)
+    m_hash = re.search(r"kernel_code_digest:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_sources_digest():
+    code = kernel_code_digest()
+    if not m_hash or not m_bytes or code is None or m_hash.group(1) != code:
         return None
     return float(m_bytes.group(1))
 
