@@ -16,6 +16,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
+// Lane l together with lane l ^ 16 (swap16) or lane l ^ 32 (swap32) of a
+// wave64, through the gfx950 cross-lane swaps instead of an LDS permute: the
+// swap exchanges 16-lane rows (or 32-lane halves) between two registers, so
+// after swapping two copies of x one copy holds every lane's own value and the
+// other its partner's, in an order that depends on the lane (checked on the
+// GPU lane by lane).  Max and sum of the pair are then the same on both lanes
+// of it.  Every lane of the wave must be active.  The swaps are written in asm
+// with both registers as in-out operands: the compiler's builtin returns the
+// first register's result for both of its outputs.  The nops give the wait
+// states around a swap of registers that a VALU instruction has just written.
+__device__ __forceinline__ void swap16(float x, float &a, float &b) {
+    a = x;
+    b = x;
+    __asm__("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float x, float &a, float &b) {
+    a = x;
+    b = x;
+    __asm__("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+    float a, b;
+    swap32(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    float a, b;
+    swap32(x, a, b);
+    return a + b;
+}
+
 // Query columns one decode workgroup holds: G query heads x q_len drafted
 // tokens, in blocks of 16 MFMA columns.  At most kMaxColumns of them, and
 // columns x Hsz at most kMaxColumnElems (their output accumulators live in

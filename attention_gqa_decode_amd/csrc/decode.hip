@@ -80,14 +80,17 @@ __device__ __forceinline__ i16x4 v_cols(const uint16_t *stage, int rs, int key0,
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
 }
 
+// Max and sum of a column's value over the four 16-lane groups.
 __device__ __forceinline__ float wave_max_over_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    float a, b;
+    swap16(x, a, b);
+    return pair_max32(fmaxf(a, b));
 }
 
 __device__ __forceinline__ float wave_sum_over_groups(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    float a, b;
+    swap16(x, a, b);
+    return pair_sum32(a + b);
 }
 
 // Launch shape for head dimension HSZ and NCB blocks of 16 MFMA columns (the

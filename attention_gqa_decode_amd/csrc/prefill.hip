@@ -250,7 +250,7 @@ void prefill_causal_kernel(
             for (int kt = 0; kt < PF_NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+            mx = pair_max32(mx) * scale_log2;
             // The reference max moves only when the block max exceeds it by more
             // than kLazy (log2 units): the weights then stay <= 2^kLazy, far inside
             // fp16, and O and l are rescaled only on the rare blocks that move it.
@@ -297,7 +297,7 @@ void prefill_causal_kernel(
     }
 
     // ---- epilogue: O = O^T / l, rounded to bf16 once ----
-    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float lt = pair_sum32(l_run);
     const int row = q0 + l32;
     if (row < ISL) {
         const float inv = 1.f / lt;
