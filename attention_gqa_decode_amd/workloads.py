@@ -180,14 +180,23 @@ def paged_layout(k: torch.Tensor, v: torch.Tensor, seqlens, block_size: int, see
     table = np.full((B, mb), -1, dtype=np.int32)
     kp = torch.zeros((total, KH, block_size, Hsz), dtype=k.dtype, device=k.device)
     vp = torch.zeros_like(kp)
-    o = 0
-    for b in range(B):
-        for i in range(nb[b]):
-            blk = int(perm[o])
-            o += 1
-            table[b, i] = blk
-            n = min(block_size, int(seqlens[b]) - i * block_size)
-            kp[blk, :, :n] = k[b, :, i * block_size:i * block_size + n]
-            vp[blk, :, :n] = v[b, :, i * block_size:i * block_size + n]
+    # logical blocks in request order (b, then i) take perm[0], perm[1], ...
+    bi = [(b, i) for b in range(B) for i in range(nb[b])]
+    if bi:
+        for o, (b, i) in enumerate(bi):
+            table[b, i] = perm[o]
+        nmax = max(nb)
+        rows = nmax * block_size  # every request's blocks, zero past its length
+        keep = torch.arange(rows, device=k.device)[None, :] < torch.tensor([int(L) for L in seqlens],
+                                                                           device=k.device)[:, None]
+        dst = torch.from_numpy(perm[:len(bi)].astype(np.int64)).to(k.device)
+        src_b = torch.tensor([b for b, _ in bi], device=k.device)
+        src_i = torch.tensor([i for _, i in bi], device=k.device)
+        for pool, x in ((kp, k), (vp, v)):
+            xp = torch.zeros((B, KH, rows, Hsz), dtype=x.dtype, device=x.device)
+            n = min(rows, S)
+            xp[:, :, :n] = torch.where(keep[:, None, :n, None], x[:, :, :n], torch.zeros((), dtype=x.dtype, device=x.device))
+            blocks = xp.view(B, KH, nmax, block_size, Hsz).permute(0, 2, 1, 3, 4)  # [B][block][KH][bs][Hsz]
+            pool[dst] = blocks[src_b, src_i]
     return kp, vp, torch.from_numpy(table).to(k.device)
 

@@ -442,6 +442,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--headline-only", action="store_true", help="time only the headline decode workload")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="omit the paged-cache runs (their setup scatters the cache block by block)")
     ap.add_argument("--workload", default="ragged",
                     help="decode workload of the headline line (ragged, llama3_8b, long_mqa, long_mqa_x8, tiny)")
     args = ap.parse_args()
@@ -485,7 +487,7 @@ def main():
             o = bench_decode(W.decode_workload(name), args.steps, args.warmup, hev)
             log(f"  {o['us_per_step']:.1f} us/step, {o['GBps']:.0f} GB/s")
             others.append(o)
-            if name == "llama3_8b":
+            if name == "llama3_8b" and not args.no_paged:
                 for bsz in (16, 64):
                     log(f"decode llama3_8b over a paged cache, block size {bsz} ...")
                     o = bench_decode(W.decode_workload("llama3_8b"), args.steps, args.warmup, hev, block_size=bsz)
