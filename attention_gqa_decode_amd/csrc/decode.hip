@@ -94,7 +94,7 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
 }
 
 // Launch shape for head dimension HSZ and NCB blocks of 16 MFMA columns (the
-// query columns: G heads x q_len drafted tokens, up to 16 NCB of them).
+// query columns: G heads x q_len drafted tokens, at most 16 x NCB of them).
 //  * KPB keys per wave block: 32, or 16 at HSZ = 256 (so one block is 16 KiB
 //    of bf16 K+V there and its staging takes 64 registers per lane), with 64
 //    columns at HSZ = 128 (whose accumulators leave no room for more), and for
