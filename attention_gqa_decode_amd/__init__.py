@@ -415,9 +415,13 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seqlens, out=None, *, scal
     """Decode over a paged KV cache (``attn_decode_ex`` with a block table).
 
     k_pool, v_pool: [num_blocks][KH][block_size][Hsz] (bf16 or FP8 E4M3 codes);
-    block_table: int32 CUDA tensor [B][max_blocks_per_seq] of block ids.
+    block_table: int32 CUDA tensor [B][max_blocks_per_seq] of block ids.  ``q`` is
+    [B][Hq][Hsz], or [B][Hq][gamma][Hsz] for multi-token decode (the drafted tokens are the
+    last gamma keys of each context; the output is then [B][Hq][gamma][Hsz]).
     """
-    a, keep = _decode_args(q, k_pool, v_pool, seqlens, out, q_len=1, multi=False, paged=True, block_table=block_table,
+    multi = q.dim() == 4
+    q_len = q.shape[2] if multi else 1
+    a, keep = _decode_args(q, k_pool, v_pool, seqlens, out, q_len=q_len, multi=multi, paged=True, block_table=block_table,
                            scale=scale, tile_keys=tile_keys, num_ctas=num_ctas, schedule=schedule,
                            num_splits=num_splits, k_scale=k_scale, v_scale=v_scale, out_lse=None, workspace=None)
     _check(lib().attn_decode_ex(ctypes.byref(a), _stream_handle(stream)))
