@@ -94,3 +94,23 @@ def test_full_size_sampled_rows():
     picks = list(range(0, 64)) + list(range(s.ISL - 64, s.ISL)) + rng.choice(s.ISL, 64, replace=False).tolist()
     rows = np.array([h * s.ISL + i for h in heads for i in picks])
     run_and_check(s.B, s.ISL, s.Hq, s.KH, s.Hsz, seed=s.seed, rows=rows)
+
+
+def draw_prefill(i):
+    """A seeded random prefill: batch, group size (odd ones too), kv heads, head dimension
+    and prompt length, so that both work orders (kv-head pairs a multiple of the 8 XCDs or
+    not) and ragged last blocks come up."""
+    rng = np.random.default_rng(6100 + i)
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    KH = int(rng.choice([1, 2, 3, 4, 8]))
+    B = int(rng.integers(1, 4))
+    Hsz = int(rng.choice([64, 128, 256]))
+    ISL = int(rng.integers(1, 600))
+    return B, ISL, G * KH, KH, Hsz
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(i):
+    B, ISL, Hq, KH, Hsz = draw_prefill(i)
+    note(f"prefill random case {i}: B={B} ISL={ISL} Hq={Hq} KH={KH} Hsz={Hsz}")
+    run_and_check(B, ISL, Hq, KH, Hsz, seed=6200 + i)
