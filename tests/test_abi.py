@@ -247,3 +247,11 @@ def test_workspace_check_uses_the_clamped_cta_count():
     a, _sl = ex_args(seqlens=(4096, 4096), num_ctas=64, tile_keys=256, schedule=A.ATTN_SCHEDULE_STREAM_K,
                      workspace=FAKE, workspace_bytes=32768 + 8192)
     assert A.lib().attn_decode_ex(ctypes.byref(a), None) == A.ATTN_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback path: without the built HIP library every entry point stops at lib()
+    monkeypatch.setattr(A, "_lib", None)
+    monkeypatch.setattr(A, "LIB_PATH", str(tmp_path / "libattn_gqa.so"))
+    with pytest.raises(RuntimeError, match="is missing"):
+        A.lib()
